@@ -1,0 +1,175 @@
+"""Seeded synthetic inputs for the routed-expert MoE layer.
+
+This module only draws random inputs; it holds none of the layer's
+arithmetic.  Both the fp64 oracle (tests, CPU baseline) and the HIP path
+(tests, benchmark) take their inputs from here.
+
+Shapes and distributions follow the workload the pages describe (896 routed
+experts, 16 active per token, single-token greedy decode: fiv.co.kr
+"kimi-k3-in-c deep dive", glossary "MoE" row and the cost paragraph;
+repolode.com "O que e?").  The pages never state d_model or d_ff; the layer
+here uses d_model = 7168 and d_ff = 2048 per expert, and a tiny layer
+(256 / 128, 16 experts, top-2) for fast exact checks.
+
+Every tensor is drawn from its own ``SeedSequence([MAGIC, layer, tensor,
+index])`` so any single expert or token can be regenerated alone:
+``index`` is the expert id for weights and the token / repetition id for x.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+MAGIC = 0x4B334D4F
+
+# tensor ids inside the seed sequence
+T_ROUTER, T_GATE_CODES, T_GATE_SCALES, T_UP_CODES, T_UP_SCALES = 0, 1, 2, 3, 4
+T_DOWN_CODES, T_DOWN_SCALES, T_X, T_RANKING = 5, 6, 7, 8
+
+SCALE_LO, SCALE_HI = 120, 124  # E8M0 scale bytes drawn uniformly in [120, 124]
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerShape:
+    name: str
+    d: int        # d_model
+    f: int        # d_ff per expert
+    E: int        # routed experts
+    k: int        # experts per token
+    layer: int    # seed-sequence layer id
+
+    @property
+    def expert_bytes(self) -> int:
+        """MX bytes of one expert: three matrices of d*f params, 4 bits each
+        plus one scale byte per 32 params."""
+        p = self.d * self.f
+        return 3 * (p // 2 + p // 32)
+
+
+TINY = LayerShape("tiny", d=256, f=128, E=16, k=2, layer=0)
+K3 = LayerShape("k3", d=7168, f=2048, E=896, k=16, layer=1)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    shape: LayerShape
+    T: int
+    act_mode: str          # "fp32" or "mxfp4"
+    zipf_bias: bool = False
+    reps: int = 1
+
+
+WORKLOADS = {
+    "tiny_decode_t1": Workload("tiny_decode_t1", TINY, T=1, act_mode="fp32", reps=1000),
+    "k3_decode_t1": Workload("k3_decode_t1", K3, T=1, act_mode="fp32", reps=1000),
+    "k3_batch_t64": Workload("k3_batch_t64", K3, T=64, act_mode="fp32", reps=100),
+    "k3_prefill_t4096": Workload("k3_prefill_t4096", K3, T=4096, act_mode="mxfp4", reps=20),
+    "k3_skew_t256": Workload("k3_skew_t256", K3, T=256, act_mode="mxfp4", zipf_bias=True, reps=100),
+}
+
+
+def rng(layer: int, tensor: int, index: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([MAGIC, layer, tensor, index]))
+
+
+def router_weight(shape: LayerShape) -> np.ndarray:
+    """W_r fp32 [E, d], entries ~ N(0, 1/d); row e from its own stream."""
+    w = np.empty((shape.E, shape.d), dtype=np.float32)
+    sd = 1.0 / math.sqrt(shape.d)
+    for e in range(shape.E):
+        w[e] = (rng(shape.layer, T_ROUTER, e).standard_normal(shape.d) * sd).astype(np.float32)
+    return w
+
+
+def token(shape: LayerShape, index: int) -> np.ndarray:
+    """One activation row, fp32 [d], entries ~ N(0, 1)."""
+    return rng(shape.layer, T_X, index).standard_normal(shape.d).astype(np.float32)
+
+
+def tokens(shape: LayerShape, T: int, first: int = 0) -> np.ndarray:
+    return np.stack([token(shape, first + t) for t in range(T)]) if T else np.zeros((0, shape.d), np.float32)
+
+
+def zipf_bias(shape: LayerShape) -> np.ndarray:
+    """Per-expert bias 2.0 * ln(1 / rank^1.1) over a seeded random ranking
+    (rank 1..E), computed in fp64 and stored fp32: a few experts draw most
+    tokens."""
+    perm = rng(shape.layer, T_RANKING, 0).permutation(shape.E)
+    rank = np.empty(shape.E, dtype=np.float64)
+    rank[perm] = np.arange(1, shape.E + 1, dtype=np.float64)
+    return (2.0 * np.log(1.0 / rank ** 1.1)).astype(np.float32)
+
+
+_MATS = {  # which: (codes tensor id, scales tensor id, rows, cols) as functions of the shape
+    "gate": (T_GATE_CODES, T_GATE_SCALES, "f", "d"),
+    "up": (T_UP_CODES, T_UP_SCALES, "f", "d"),
+    "down": (T_DOWN_CODES, T_DOWN_SCALES, "d", "f"),
+}
+
+
+def expert_matrix(shape: LayerShape, e: int, which: str):
+    """One MX matrix of expert e: (codes u8 [rows, cols/2], scales u8
+    [rows, cols/32]).  Codes are uniform bytes (every 4-bit code equally
+    likely, including -0); scale bytes uniform in [120, 124]."""
+    tc, ts, r, c = _MATS[which]
+    rows, cols = getattr(shape, r), getattr(shape, c)
+    codes = rng(shape.layer, tc, e).integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    scales = rng(shape.layer, ts, e).integers(SCALE_LO, SCALE_HI + 1, size=(rows, cols // 32), dtype=np.uint8)
+    return codes, scales
+
+
+def expert(shape: LayerShape, e: int) -> dict:
+    return {w: expert_matrix(shape, e, w) for w in ("gate", "up", "down")}
+
+
+def all_experts_host(shape: LayerShape, threads: int = 8) -> dict:
+    """Every expert's matrices stacked: {which: (codes [E, rows, cols/2],
+    scales [E, rows, cols/32])}.  Only for small shapes (the full layer is
+    21 GB; use ``upload_experts`` for that)."""
+    out = {}
+    for which in ("gate", "up", "down"):
+        _, _, r, c = _MATS[which]
+        rows, cols = getattr(shape, r), getattr(shape, c)
+        codes = np.empty((shape.E, rows, cols // 2), np.uint8)
+        scales = np.empty((shape.E, rows, cols // 32), np.uint8)
+
+        def fill(e, which=which, codes=codes, scales=scales):
+            codes[e], scales[e] = expert_matrix(shape, e, which)
+
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, range(shape.E)))
+        out[which] = (codes, scales)
+    return out
+
+
+def upload_experts(shape: LayerShape, device, threads: int = 16, experts=None) -> dict:
+    """Generate every expert on the host, expert by expert in a thread pool,
+    and copy each into preallocated device tensors.  Returns {which: (codes,
+    scales)} as torch uint8 tensors on ``device`` with shapes
+    [E, rows, cols/2] and [E, rows, cols/32].  ``experts`` optionally limits
+    generation to a subset (the rest stay zero)."""
+    import torch
+
+    out = {}
+    for which in ("gate", "up", "down"):
+        _, _, r, c = _MATS[which]
+        rows, cols = getattr(shape, r), getattr(shape, c)
+        out[which] = (torch.zeros((shape.E, rows, cols // 2), dtype=torch.uint8, device=device),
+                      torch.zeros((shape.E, rows, cols // 32), dtype=torch.uint8, device=device))
+    ids = range(shape.E) if experts is None else sorted(set(int(e) for e in experts))
+
+    def job(e):
+        return e, expert(shape, e)
+
+    ids = list(ids)
+    with ThreadPoolExecutor(threads) as ex:
+        for c0 in range(0, len(ids), 2 * threads):  # bounded host memory
+            for e, mats in ex.map(job, ids[c0:c0 + 2 * threads]):
+                for which, (cd, sc) in mats.items():
+                    out[which][0][e].copy_(torch.from_numpy(cd))
+                    out[which][1][e].copy_(torch.from_numpy(sc))
+    return out
