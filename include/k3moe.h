@@ -1,0 +1,166 @@
+/*
+ * k3moe.h -- C ABI of the MI355X (gfx950) routed-expert MoE layer.
+ *
+ * The layer (the routed-expert half of one MoE layer of the pages' 2.78T
+ * model; fiv.co.kr "kimi-k3-in-c deep dive", sections "four reductions" and
+ * the glossary rows "MoE" and "MXFP4"):
+ *
+ *   route:   l[t,e] = x[t] . Wr[e]  (fp64 accumulation)           (+ bias)
+ *            S_t    = the k experts with the largest selection key,
+ *                     ties to the lower expert index, listed in that order
+ *            w[t,j] = softmax over all experts, restricted to S_t and
+ *                     renormalised to sum to one
+ *            grouping of the T*k token-expert pairs by expert
+ *   ffn:     for each pair (t, e = S_t[j]):
+ *              h = silu(Wg_e x_t) * (Wu_e x_t)      (SwiGLU, d -> f)
+ *              o = Wd_e h                           (f -> d)
+ *            y[t] = sum_j w[t,j] * o_{t,j}
+ *
+ * computed directly on MXFP4 weights: 4-bit E2M1 codes with one E8M0 scale
+ * per 32 consecutive values, value = E2M1[code] * 2^(scale - 127)
+ * (fiv.co.kr deep dive, "four reductions", MXFP4 note; the weights are never
+ * expanded to a wider format in memory).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named as device pointers must be device memory of the current
+ *    HIP device (e.g. torch tensors); the caller owns all of them.  The
+ *    library allocates nothing and keeps no state between calls except a
+ *    per-device cache of "is this device gfx950".
+ *  - Calls only enqueue work on `stream` and never synchronise; outputs are
+ *    valid once the stream has completed that work.  Calls that share a
+ *    workspace must be ordered on one stream.
+ *  - Every argument is checked on the host before any HIP call or launch;
+ *    errors are returned as negative K3MOE_E* codes, never thrown.  Unknown
+ *    enumeration values are refused, never defaulted.
+ *  - T == 0 is a valid no-op that returns K3MOE_OK.
+ */
+#ifndef K3MOE_H
+#define K3MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define K3MOE_OK          0
+#define K3MOE_EINVAL     -1  /* bad dimension, null or misaligned pointer    */
+#define K3MOE_EWORKSPACE -2  /* workspace missing or smaller than required   */
+#define K3MOE_ENOTSUP    -3  /* unknown mode, E > 1024, k > 32, not gfx950   */
+#define K3MOE_EHIP       -4  /* a HIP call or launch failed; see last_hip_error */
+
+/* ---- modes --------------------------------------------------------------- */
+/* Router bias.  The pages' router steers only the *selection* with its bias
+ * and weights the chosen experts by unbiased scores (fiv.co.kr deep dive,
+ * invariant #5).  K3MOE_BIAS_LOGITS instead adds the bias to the logits, so it
+ * moves both the choice and the weights. */
+#define K3MOE_BIAS_NONE         0  /* bias ignored (may be NULL)             */
+#define K3MOE_BIAS_LOGITS       1  /* l += b: selection and weights          */
+#define K3MOE_BIAS_SELECT_ONLY  2  /* key = l + b for selection; weights from l */
+
+/* Activation precision inside the expert FFN. */
+#define K3MOE_ACT_FP32   0  /* x and h stay fp32; weights decoded on the fly  */
+#define K3MOE_ACT_MXFP4  1  /* x quantised per token, h per pair, to MXFP4 (OCP
+                               MX rule: scale 2^(floor(log2 amax) - 2), codes
+                               round-to-nearest-even, saturating at 6), then
+                               scaled-MXFP4 matrix-core products            */
+
+/* ---- shapes ------------------------------------------------------------ */
+typedef struct {
+    int32_t T;        /* tokens, >= 0                                         */
+    int32_t E;        /* routed experts, 1..1024                              */
+    int32_t k;        /* experts per token, 1..min(E, 32)                     */
+    int32_t d_model;  /* > 0, multiple of 32                                  */
+    int32_t d_ff;     /* > 0, multiple of 32                                  */
+} k3moe_dims;
+
+/* One MX matrix [rows][cols] (blocks of 32 along cols, the reduction axis):
+ *   codes  : uint8 [rows][cols/2], element 2i in the low nibble of byte i,
+ *            element 2i+1 in the high nibble; 16-byte aligned
+ *   scales : uint8 [rows][cols/32], E8M0 (255 = NaN is outside the contract)
+ * Rows are contiguous with no padding: a matrix of P values takes
+ * P/2 + P/32 bytes (0.53125 B/param, the pages' per-expert byte count). */
+typedef struct {
+    const uint8_t *codes;
+    const uint8_t *scales;
+} k3moe_mx;
+
+/* All experts, stacked along a leading expert axis:
+ *   gate, up : [E][d_ff][d_model]   (h = silu(gate x) * up x)
+ *   down     : [E][d_model][d_ff]                                          */
+typedef struct {
+    k3moe_mx gate, up, down;
+} k3moe_experts;
+
+/* Optional intermediates of the MXFP4 activation path (all device memory,
+ * any field may be NULL; ignored in K3MOE_ACT_FP32 mode).  Pair index
+ * p = t*k + j.
+ *   x_codes  [T][d_model/2], x_scales [T][d_model/32] : MX(x) per token
+ *   h        [T*k][d_ff] fp32 : silu(g)*u before quantisation, per pair
+ *   h_codes  [T*k][d_ff/2], h_scales [T*k][d_ff/32]   : MX(h) per pair     */
+typedef struct {
+    uint8_t *x_codes;
+    uint8_t *x_scales;
+    float   *h;
+    uint8_t *h_codes;
+    uint8_t *h_scales;
+} k3moe_debug;
+
+/* Bytes of device workspace the calls need for these dimensions and
+ * activation mode (a pure host computation; no HIP call).  One workspace of
+ * this size serves k3moe_route, k3moe_ffn and k3moe_forward. */
+int k3moe_workspace_size(const k3moe_dims *dims, int act_mode, size_t *bytes);
+
+/* Router and grouping (all device pointers):
+ *   x         fp32 [T][d_model]           (16-byte aligned)
+ *   w_router  fp32 [E][d_model]           (16-byte aligned)
+ *   bias      fp32 [E] or NULL (required unless bias_mode == BIAS_NONE)
+ * outputs (bit-deterministic):
+ *   topk_idx    int32 [T][k]  chosen experts, descending key, ties -> lower id
+ *   topk_w      fp32  [T][k]  renormalised softmax weights (sum to 1)
+ *   counts      int32 [E]     tokens per expert
+ *   offsets     int32 [E+1]   exclusive prefix sum of counts
+ *   perm_pair   int32 [T*k]   row -> pair t*k+j; rows grouped by expert in
+ *                             ascending expert id, tokens ascending inside
+ *   row_of_pair int32 [T*k]   inverse of perm_pair
+ * ws: device workspace of at least k3moe_workspace_size() bytes, 256-aligned. */
+int k3moe_route(const k3moe_dims *dims, const float *x, const float *w_router,
+                const float *bias, int bias_mode,
+                int32_t *topk_idx, float *topk_w, int32_t *counts,
+                int32_t *offsets, int32_t *perm_pair, int32_t *row_of_pair,
+                void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expert FFN and combine, from the outputs of k3moe_route (device pointers).
+ *   y  fp32 [T][d_model], fully overwritten.
+ *   dbg optional (NULL or a host struct of device pointers), MXFP4 mode only.
+ * In K3MOE_ACT_FP32 mode y is bit-deterministic; in K3MOE_ACT_MXFP4 mode the
+ * combine is a scatter-add whose fp32 summation order may vary run to run. */
+int k3moe_ffn(const k3moe_dims *dims, const float *x, const k3moe_experts *experts,
+              const int32_t *topk_idx, const float *topk_w, const int32_t *counts,
+              const int32_t *offsets, const int32_t *perm_pair,
+              const int32_t *row_of_pair, int act_mode, float *y,
+              const k3moe_debug *dbg, void *ws, size_t ws_bytes,
+              hipStream_t stream);
+
+/* k3moe_route followed by k3moe_ffn on the same stream and workspace; every
+ * routing output is still written (the caller owns those buffers). */
+int k3moe_forward(const k3moe_dims *dims, const float *x, const float *w_router,
+                  const float *bias, int bias_mode, const k3moe_experts *experts,
+                  int act_mode, int32_t *topk_idx, float *topk_w,
+                  int32_t *counts, int32_t *offsets, int32_t *perm_pair,
+                  int32_t *row_of_pair, float *y, const k3moe_debug *dbg,
+                  void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Human-readable text of a status code (static storage). */
+const char *k3moe_status_string(int status);
+
+/* hipError_t of the last K3MOE_EHIP returned on this host thread (0 if none). */
+int k3moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* K3MOE_H */

@@ -1,0 +1,325 @@
+// api.hip -- the C ABI (include/k3moe.h): host-side argument checks,
+// workspace carve-up and the launch sequence of the routed-expert MoE layer.
+//
+// Arguments are refused, never defaulted, when they are out of contract (the
+// pages' configuration reader likewise refuses unknown fields instead of
+// guessing: fiv.co.kr "kimi-k3-in-c deep dive", the study-plan row on
+// correctness and reproducibility).  All checks run before the first HIP call.
+#include <string.h>
+#include <atomic>
+#include "k3moe.h"
+#include "kernels.h"
+
+namespace k3 {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(int T, int E, int k, int d, int f, int act_mode)
+{
+    WsLayout L{};
+    const size_t P = (size_t)T * k;
+    const size_t nch = ((size_t)T + kChunk - 1) / kChunk;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
+    L.logits = take((size_t)T * E * sizeof(double));
+    L.chunk_masks = take(nch * E * sizeof(uint64_t));
+    L.chunk_base = take(nch * E * sizeof(int32_t));
+    L.active = take(((size_t)E + 1) * sizeof(int32_t));
+    L.route_total = off;
+    if (act_mode == K3MOE_ACT_FP32) {
+        L.h = take(P * f * sizeof(float));
+        L.o = take(P * d * sizeof(float));
+    } else {
+        L.xq_codes = take((size_t)T * d / 2);
+        L.xq_scales = take((size_t)T * d / 32);
+        L.hq_codes = take(P * f / 2);
+        L.hq_scales = take(P * f / 32);
+    }
+    L.total = off;
+    return L;
+}
+
+}  // namespace k3
+
+using namespace k3;
+
+static thread_local int g_last_hip_error = 0;
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static int check_dims(const k3moe_dims* dm)
+{
+    if (!dm) return K3MOE_EINVAL;
+    if (dm->T < 0 || dm->E < 1 || dm->k < 1 || dm->k > dm->E) return K3MOE_EINVAL;
+    if (dm->d_model <= 0 || dm->d_ff <= 0 || dm->d_model % 32 || dm->d_ff % 32) return K3MOE_EINVAL;
+    if ((int64_t)dm->T * dm->k > INT32_MAX) return K3MOE_EINVAL;
+    if ((int64_t)dm->T * dm->k * (int64_t)(dm->d_model > dm->d_ff ? dm->d_model : dm->d_ff) >
+        ((int64_t)1 << 40))
+        return K3MOE_EINVAL;  // row offsets must fit the kernels' index arithmetic
+    if (dm->E > 1024 || dm->k > 32) return K3MOE_ENOTSUP;
+    return K3MOE_OK;
+}
+
+static int check_mode_act(int act_mode)
+{
+    return (act_mode == K3MOE_ACT_FP32 || act_mode == K3MOE_ACT_MXFP4) ? K3MOE_OK : K3MOE_ENOTSUP;
+}
+
+static int check_mode_bias(int bias_mode, const float* bias)
+{
+    if (bias_mode != K3MOE_BIAS_NONE && bias_mode != K3MOE_BIAS_LOGITS &&
+        bias_mode != K3MOE_BIAS_SELECT_ONLY)
+        return K3MOE_ENOTSUP;
+    if (bias_mode != K3MOE_BIAS_NONE && !bias) return K3MOE_EINVAL;
+    return K3MOE_OK;
+}
+
+// act_mode < 0: only the routing part of the workspace is needed
+static int check_ws(const k3moe_dims* dm, int act_mode, const void* ws, size_t ws_bytes)
+{
+    WsLayout L = ws_layout(dm->T, dm->E, dm->k, dm->d_model, dm->d_ff,
+                           act_mode < 0 ? K3MOE_ACT_MXFP4 : act_mode);
+    size_t need = act_mode < 0 ? L.route_total : L.total;
+    if (!ws || ws_bytes < need) return K3MOE_EWORKSPACE;
+    if (!aligned(ws, 256)) return K3MOE_EINVAL;
+    return K3MOE_OK;
+}
+
+static int check_mx(const k3moe_mx& m)
+{
+    if (!m.codes || !m.scales) return K3MOE_EINVAL;
+    if (!aligned(m.codes, 16) || !aligned(m.scales, 4)) return K3MOE_EINVAL;
+    return K3MOE_OK;
+}
+
+// Cached per device: 1 = gfx950, -1 = other, 0 = unknown yet.
+static std::atomic<int> g_is_gfx950[64];
+
+static int check_device()
+{
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return K3MOE_EHIP;
+    }
+    if (dev < 0 || dev >= 64) return K3MOE_ENOTSUP;
+    int v = g_is_gfx950[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        hipDeviceProp_t prop;
+        err = hipGetDeviceProperties(&prop, dev);
+        if (err != hipSuccess) {
+            g_last_hip_error = (int)err;
+            return K3MOE_EHIP;
+        }
+        v = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+        g_is_gfx950[dev].store(v, std::memory_order_relaxed);
+    }
+    return v == 1 ? K3MOE_OK : K3MOE_ENOTSUP;
+}
+
+static int finish_launches()
+{
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return K3MOE_EHIP;
+    }
+    return K3MOE_OK;
+}
+
+// ---------------------------------------------------------------- checks ---
+static int validate_route(const k3moe_dims* dm, const float* x, const float* w_router,
+                          const float* bias, int bias_mode, int32_t* topk_idx, float* topk_w,
+                          int32_t* counts, int32_t* offsets, int32_t* perm_pair,
+                          int32_t* row_of_pair, void* ws, size_t ws_bytes, int act_mode_for_ws)
+{
+    int rc = check_dims(dm);
+    if (rc) return rc;
+    if ((rc = check_mode_bias(bias_mode, bias))) return rc;
+    if (dm->T == 0) return K3MOE_OK;
+    if (!x || !w_router || !topk_idx || !topk_w || !counts || !offsets || !perm_pair || !row_of_pair)
+        return K3MOE_EINVAL;
+    if (!aligned(x, 16) || !aligned(w_router, 16)) return K3MOE_EINVAL;
+    return check_ws(dm, act_mode_for_ws, ws, ws_bytes);
+}
+
+static int validate_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts* ex,
+                        const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
+                        const int32_t* offsets, const int32_t* perm_pair, const int32_t* row_of_pair,
+                        int act_mode, float* y, void* ws, size_t ws_bytes)
+{
+    int rc = check_dims(dm);
+    if (rc) return rc;
+    if ((rc = check_mode_act(act_mode))) return rc;
+    if (dm->T == 0) return K3MOE_OK;
+    if (!x || !ex || !topk_idx || !topk_w || !counts || !offsets || !perm_pair || !row_of_pair || !y)
+        return K3MOE_EINVAL;
+    if (!aligned(x, 16) || !aligned(y, 16)) return K3MOE_EINVAL;
+    if ((rc = check_mx(ex->gate)) || (rc = check_mx(ex->up)) || (rc = check_mx(ex->down))) return rc;
+    return check_ws(dm, act_mode, ws, ws_bytes);
+}
+
+// --------------------------------------------------------------- enqueue ---
+static void enqueue_route(const k3moe_dims* dm, const float* x, const float* w_router,
+                          const float* bias, int bias_mode, int32_t* topk_idx, float* topk_w,
+                          int32_t* counts, int32_t* offsets, int32_t* perm_pair,
+                          int32_t* row_of_pair, char* ws, const WsLayout& L, hipStream_t s)
+{
+    double* logits = reinterpret_cast<double*>(ws + L.logits);
+    launch_router_logits(dm->T, dm->E, dm->d_model, x, w_router, bias,
+                         bias_mode == K3MOE_BIAS_LOGITS, logits, s);
+    launch_topk_group(dm->T, dm->E, dm->k, logits, bias, bias_mode == K3MOE_BIAS_SELECT_ONLY,
+                      topk_idx, topk_w, reinterpret_cast<uint64_t*>(ws + L.chunk_masks),
+                      reinterpret_cast<int32_t*>(ws + L.chunk_base), counts, offsets, perm_pair,
+                      row_of_pair, s);
+}
+
+static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts* ex,
+                        const int32_t* topk_idx, const float* topk_w, const int32_t* offsets,
+                        const int32_t* perm_pair, const int32_t* row_of_pair, int act_mode,
+                        float* y, const k3moe_debug* dbg, char* ws, const WsLayout& L,
+                        hipStream_t s)
+{
+    FfnArgs a{};
+    a.T = dm->T;
+    a.E = dm->E;
+    a.k = dm->k;
+    a.d = dm->d_model;
+    a.f = dm->d_ff;
+    a.P = dm->T * dm->k;
+    a.x = x;
+    a.gc = ex->gate.codes;
+    a.gs = ex->gate.scales;
+    a.uc = ex->up.codes;
+    a.us = ex->up.scales;
+    a.dc = ex->down.codes;
+    a.ds = ex->down.scales;
+    a.topk_idx = topk_idx;
+    a.topk_w = topk_w;
+    a.offsets = offsets;
+    a.perm_pair = perm_pair;
+    a.row_of_pair = row_of_pair;
+    if (a.P <= a.E) {
+        // few pairs: a slot per grouped row, the segment heads do the work
+        a.active = nullptr;
+        a.nslots = a.P;
+    } else {
+        int32_t* active = reinterpret_cast<int32_t*>(ws + L.active);
+        launch_active_list(a.E, offsets, active, s);
+        a.active = active;
+        a.nslots = a.E;
+    }
+    if (act_mode == K3MOE_ACT_FP32) {
+        float* h = reinterpret_cast<float*>(ws + L.h);
+        float* o = reinterpret_cast<float*>(ws + L.o);
+        launch_gateup_gemv(a, h, s);
+        launch_down_gemv(a, h, o, s);
+        launch_combine(a, o, y, s);
+    } else {
+        uint8_t* xqc = reinterpret_cast<uint8_t*>(ws + L.xq_codes);
+        uint8_t* xqs = reinterpret_cast<uint8_t*>(ws + L.xq_scales);
+        uint8_t* hqc = reinterpret_cast<uint8_t*>(ws + L.hq_codes);
+        uint8_t* hqs = reinterpret_cast<uint8_t*>(ws + L.hq_scales);
+        launch_quantize_rows((long)a.T * (a.d / 32), x, xqc, xqs, s);
+        hipError_t err = hipSuccess;
+        if (dbg && dbg->x_codes && err == hipSuccess)
+            err = hipMemcpyAsync(dbg->x_codes, xqc, (size_t)a.T * a.d / 2, hipMemcpyDeviceToDevice, s);
+        if (dbg && dbg->x_scales && err == hipSuccess)
+            err = hipMemcpyAsync(dbg->x_scales, xqs, (size_t)a.T * a.d / 32, hipMemcpyDeviceToDevice, s);
+        if (err != hipSuccess) {
+            g_last_hip_error = (int)err;
+            return K3MOE_EHIP;
+        }
+        launch_gateup_mfma(a, xqc, xqs, hqc, hqs, dbg ? dbg->h : nullptr,
+                           dbg ? dbg->h_codes : nullptr, dbg ? dbg->h_scales : nullptr, s);
+        launch_zero(y, (size_t)a.T * a.d, s);
+        launch_down_mfma(a, hqc, hqs, y, s);
+    }
+    return K3MOE_OK;
+}
+
+extern "C" {
+
+int k3moe_workspace_size(const k3moe_dims* dims, int act_mode, size_t* bytes)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if ((rc = check_mode_act(act_mode))) return rc;
+    if (!bytes) return K3MOE_EINVAL;
+    *bytes = ws_layout(dims->T, dims->E, dims->k, dims->d_model, dims->d_ff, act_mode).total;
+    return K3MOE_OK;
+}
+
+int k3moe_route(const k3moe_dims* dims, const float* x, const float* w_router, const float* bias,
+                int bias_mode, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                int32_t* perm_pair, int32_t* row_of_pair, void* ws, size_t ws_bytes,
+                hipStream_t stream)
+{
+    // the routing part of the workspace is identical in both activation modes
+    int rc = validate_route(dims, x, w_router, bias, bias_mode, topk_idx, topk_w, counts, offsets,
+                            perm_pair, row_of_pair, ws, ws_bytes, -1);
+    if (rc || dims->T == 0) return rc;
+    if ((rc = check_device())) return rc;
+    WsLayout L = ws_layout(dims->T, dims->E, dims->k, dims->d_model, dims->d_ff, K3MOE_ACT_MXFP4);
+    enqueue_route(dims, x, w_router, bias, bias_mode, topk_idx, topk_w, counts, offsets, perm_pair,
+                  row_of_pair, static_cast<char*>(ws), L, stream);
+    return finish_launches();
+}
+
+int k3moe_ffn(const k3moe_dims* dims, const float* x, const k3moe_experts* experts,
+              const int32_t* topk_idx, const float* topk_w, const int32_t* counts,
+              const int32_t* offsets, const int32_t* perm_pair, const int32_t* row_of_pair,
+              int act_mode, float* y, const k3moe_debug* dbg, void* ws, size_t ws_bytes,
+              hipStream_t stream)
+{
+    int rc = validate_ffn(dims, x, experts, topk_idx, topk_w, counts, offsets, perm_pair, row_of_pair,
+                          act_mode, y, ws, ws_bytes);
+    if (rc || dims->T == 0) return rc;
+    if ((rc = check_device())) return rc;
+    WsLayout L = ws_layout(dims->T, dims->E, dims->k, dims->d_model, dims->d_ff, act_mode);
+    rc = enqueue_ffn(dims, x, experts, topk_idx, topk_w, offsets, perm_pair, row_of_pair, act_mode, y,
+                     act_mode == K3MOE_ACT_MXFP4 ? dbg : nullptr, static_cast<char*>(ws), L, stream);
+    return rc ? rc : finish_launches();
+}
+
+int k3moe_forward(const k3moe_dims* dims, const float* x, const float* w_router, const float* bias,
+                  int bias_mode, const k3moe_experts* experts, int act_mode, int32_t* topk_idx,
+                  float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm_pair,
+                  int32_t* row_of_pair, float* y, const k3moe_debug* dbg, void* ws, size_t ws_bytes,
+                  hipStream_t stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if ((rc = check_mode_act(act_mode))) return rc;
+    rc = validate_route(dims, x, w_router, bias, bias_mode, topk_idx, topk_w, counts, offsets,
+                        perm_pair, row_of_pair, ws, ws_bytes, act_mode);
+    if (rc) return rc;
+    rc = validate_ffn(dims, x, experts, topk_idx, topk_w, counts, offsets, perm_pair, row_of_pair,
+                      act_mode, y, ws, ws_bytes);
+    if (rc || dims->T == 0) return rc;
+    if ((rc = check_device())) return rc;
+    WsLayout L = ws_layout(dims->T, dims->E, dims->k, dims->d_model, dims->d_ff, act_mode);
+    char* w = static_cast<char*>(ws);
+    enqueue_route(dims, x, w_router, bias, bias_mode, topk_idx, topk_w, counts, offsets, perm_pair,
+                  row_of_pair, w, L, stream);
+    rc = enqueue_ffn(dims, x, experts, topk_idx, topk_w, offsets, perm_pair, row_of_pair, act_mode, y,
+                     act_mode == K3MOE_ACT_MXFP4 ? dbg : nullptr, w, L, stream);
+    return rc ? rc : finish_launches();
+}
+
+const char* k3moe_status_string(int status)
+{
+    switch (status) {
+        case K3MOE_OK: return "ok";
+        case K3MOE_EINVAL: return "invalid argument (dimension, null or misaligned pointer)";
+        case K3MOE_EWORKSPACE: return "workspace missing or too small";
+        case K3MOE_ENOTSUP: return "not supported (mode, E > 1024, k > 32, or device is not gfx950)";
+        case K3MOE_EHIP: return "HIP error (see k3moe_last_hip_error)";
+        default: return "unknown status";
+    }
+}
+
+int k3moe_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// kernels.h -- host-side launchers of the gfx950 kernels (internal to the HIP
+// library; the public surface is include/k3moe.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace k3 {
+
+// Tokens per permutation chunk: one bit per token in a 64-bit mask.
+constexpr int kChunk = 64;
+
+// Workspace carve-up (byte offsets from the 256-aligned workspace base).
+struct WsLayout {
+    size_t logits;       // double [T][E]            router logits (+bias)
+    size_t chunk_masks;  // uint64 [nch][E]          which chunk tokens chose e
+    size_t chunk_base;   // int32  [nch][E]          rows of e before chunk c
+    size_t active;       // int32  [E + 1]           active experts, count last
+    size_t route_total;  // bytes the routing calls need (a prefix of the rest)
+    size_t h;            // fp32   [T*k][f]          fp32 mode: SwiGLU output
+    size_t o;            // fp32   [T*k][d]          fp32 mode: per-pair down
+    size_t xq_codes;     // uint8  [T][d/2]          mx mode: MX(x)
+    size_t xq_scales;    // uint8  [T][d/32]
+    size_t hq_codes;     // uint8  [T*k][f/2]        mx mode: MX(h)
+    size_t hq_scales;    // uint8  [T*k][f/32]
+    size_t total;
+};
+
+WsLayout ws_layout(int T, int E, int k, int d, int f, int act_mode);
+
+// ---- routing ------------------------------------------------------------
+void launch_router_logits(int T, int E, int d, const float* x, const float* wr,
+                          const float* bias, int bias_in_logits, double* logits,
+                          hipStream_t s);
+// top-k + weights + per-chunk masks; for T <= 64 also the whole grouping
+void launch_topk_group(int T, int E, int k, const double* logits, const float* bias,
+                       int bias_select_only, int32_t* topk_idx, float* topk_w,
+                       uint64_t* chunk_masks, int32_t* chunk_base, int32_t* counts,
+                       int32_t* offsets, int32_t* perm_pair, int32_t* row_of_pair,
+                       hipStream_t s);
+void launch_active_list(int E, const int32_t* offsets, int32_t* active, hipStream_t s);
+
+// ---- fp32-activation expert path (GEMV family) ----------------------------
+struct FfnArgs {
+    int T, E, k, d, f, P;
+    const float* x;
+    const uint8_t *gc, *gs, *uc, *us, *dc, *ds;
+    const int32_t* topk_idx;
+    const float* topk_w;
+    const int32_t* offsets;
+    const int32_t* perm_pair;
+    const int32_t* row_of_pair;
+    const int32_t* active;  // null: slots are sorted rows (segment heads)
+    int nslots;
+};
+void launch_gateup_gemv(const FfnArgs& a, float* h, hipStream_t s);
+void launch_down_gemv(const FfnArgs& a, const float* h, float* o, hipStream_t s);
+void launch_combine(const FfnArgs& a, const float* o, float* y, hipStream_t s);
+
+// ---- MXFP4-activation expert path (scaled-MFMA family) --------------------
+void launch_quantize_rows(long nblocks, const float* v, uint8_t* codes, uint8_t* scales,
+                          hipStream_t s);
+void launch_gateup_mfma(const FfnArgs& a, const uint8_t* xq_codes, const uint8_t* xq_scales,
+                        uint8_t* hq_codes, uint8_t* hq_scales, float* dbg_h,
+                        uint8_t* dbg_hc, uint8_t* dbg_hs, hipStream_t s);
+void launch_zero(float* y, size_t n, hipStream_t s);
+void launch_down_mfma(const FfnArgs& a, const uint8_t* hq_codes, const uint8_t* hq_scales,
+                      float* y, hipStream_t s);
+
+}  // namespace k3

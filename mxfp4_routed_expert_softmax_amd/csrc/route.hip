@@ -1,0 +1,362 @@
+// route.hip -- router logits (fp64), softmax top-k, and the grouping of
+// token-expert pairs by expert, for gfx950.
+//
+// The pages' router (k3_router, fiv.co.kr "kimi-k3-in-c deep dive", study-plan
+// row "MoE and routing") scores every expert, picks 16 of 896 per token
+// (glossary row "MoE") and hands the chosen experts to k3_moe.  Here the
+// scores are fp64-accumulated logits, the choice is the top-k with ties to the
+// lower expert index, and the weights are the softmax over all experts
+// restricted to the chosen ones and renormalised (equal to a softmax over the
+// chosen logits).  The grouping is a deterministic counting sort: per
+// 64-token chunk a bitmask per expert, a prefix over chunks and experts, and a
+// rank inside the chunk by popcount -- no atomics decide an order.
+#include <float.h>
+#include "device_common.h"
+#include "kernels.h"
+
+namespace k3 {
+
+// ---------------------------------------------------------------------------
+// Router logits, small T: one wave per expert row, every token of the batch
+// accumulated while the row streams through once.  fp32 x fp32 products are
+// exact in fp64; the sums are fp64.
+constexpr int kGemvTok = 8;
+
+__global__ __launch_bounds__(256) void router_gemv_kernel(
+    int T, int E, int d, const float* __restrict__ x, const float* __restrict__ wr,
+    const float* __restrict__ bias, int bias_in_logits, double* __restrict__ logits)
+{
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= E) return;
+    const float4* w4 = reinterpret_cast<const float4*>(wr + (size_t)e * d);
+    const int n4 = d >> 2;
+    double acc[kGemvTok];
+#pragma unroll
+    for (int t = 0; t < kGemvTok; ++t) acc[t] = 0.0;
+    for (int i = lane; i < n4; i += 64) {
+        float4 w = w4[i];
+#pragma unroll
+        for (int t = 0; t < kGemvTok; ++t) {
+            if (t < T) {
+                float4 v = reinterpret_cast<const float4*>(x + (size_t)t * d)[i];
+                acc[t] = fma((double)w.x, (double)v.x, acc[t]);
+                acc[t] = fma((double)w.y, (double)v.y, acc[t]);
+                acc[t] = fma((double)w.z, (double)v.z, acc[t]);
+                acc[t] = fma((double)w.w, (double)v.w, acc[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < kGemvTok; ++t) {
+        if (t < T) {
+            double v = acc[t];
+            for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+            if (lane == 0) {
+                if (bias_in_logits) v += (double)bias[e];
+                logits[(size_t)t * E + e] = v;
+            }
+        }
+    }
+}
+
+// Router logits, larger T: 64 tokens x 64 experts per 256-thread block, each
+// thread a 4 x 4 register tile, K staged through LDS as fp64.
+__global__ __launch_bounds__(256) void router_gemm_kernel(
+    int T, int E, int d, const float* __restrict__ x, const float* __restrict__ wr,
+    const float* __restrict__ bias, int bias_in_logits, double* __restrict__ logits)
+{
+    constexpr int BK = 32;
+    __shared__ double xs[BK][64 + 1];
+    __shared__ double ws[BK][64 + 1];
+    const int tid = threadIdx.x;
+    const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
+    const int ty = tid >> 4, tx = tid & 15;  // 16 x 16 threads, 4 x 4 outputs each
+    double acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    for (int k0 = 0; k0 < d; k0 += BK) {
+        // 64 rows x 32 cols of x and of wr: 2048 values each, 8 per thread
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            int idx = tid + q * 256;
+            int r = idx >> 5, c = idx & 31;
+            int tr = t0 + r, er = e0 + r;
+            xs[c][r] = (tr < T) ? (double)x[(size_t)tr * d + k0 + c] : 0.0;
+            ws[c][r] = (er < E) ? (double)wr[(size_t)er * d + k0 + c] : 0.0;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int c = 0; c < BK; ++c) {
+            double a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = xs[c][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = ws[c][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int t = t0 + ty * 4 + i;
+        if (t >= T) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int e = e0 + tx * 4 + j;
+            if (e >= E) continue;
+            double v = acc[i][j];
+            if (bias_in_logits) v += (double)bias[e];
+            logits[(size_t)t * E + e] = v;
+        }
+    }
+}
+
+void launch_router_logits(int T, int E, int d, const float* x, const float* wr,
+                          const float* bias, int bias_in_logits, double* logits,
+                          hipStream_t s)
+{
+    if (T <= kGemvTok) {
+        router_gemv_kernel<<<dim3((E + 3) / 4), dim3(256), 0, s>>>(T, E, d, x, wr, bias,
+                                                                   bias_in_logits, logits);
+    } else {
+        router_gemm_kernel<<<dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s>>>(
+            T, E, d, x, wr, bias, bias_in_logits, logits);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide exclusive scan over blockDim.x (multiple of 64, <= 1024) ints.
+__device__ int block_exclusive_scan(int v, int* wave_tot, int* total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    int inc = v;
+    for (int m = 1; m < 64; m <<= 1) {
+        int o = __shfl_up(inc, m, 64);
+        if (lane >= m) inc += o;
+    }
+    if (lane == 63) wave_tot[wave] = inc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int w = 0; w < nw; ++w) {
+            int tmp = wave_tot[w];
+            wave_tot[w] = run;
+            run += tmp;
+        }
+        wave_tot[nw] = run;
+    }
+    __syncthreads();
+    int excl = wave_tot[wave] + inc - v;
+    *total = wave_tot[nw];
+    __syncthreads();
+    return excl;
+}
+
+// Top-k of one token held by one wave: lane l owns experts l, l+64, ...
+// (E <= 1024 -> at most 16 per lane).  k rounds of a wave-wide
+// (key max, index min) reduction; the winning lane retires its entry.
+constexpr int kMaxPerLane = 16;
+
+__device__ void wave_topk(int E, int k, const double* __restrict__ lrow,
+                          const float* __restrict__ bias, int bias_select_only,
+                          int* sel_e_out, int32_t* idx_out, float* w_out)
+{
+    const int lane = threadIdx.x & 63;
+    double key[kMaxPerLane], wl[kMaxPerLane];
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+        int e = lane + 64 * i;
+        double l = (e < E) ? lrow[e] : -DBL_MAX;
+        wl[i] = l;
+        key[i] = (e < E && bias_select_only) ? l + (double)bias[e] : l;
+    }
+    uint32_t taken = 0;
+    int my_e = 0;
+    double my_wl = 0.0;
+    for (int j = 0; j < k; ++j) {
+        double bk = 0.0, bw = 0.0;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < kMaxPerLane; ++i) {
+            int e = lane + 64 * i;
+            bool ok = (e < E) && !((taken >> i) & 1u);
+            if (ok && (be == 0x7fffffff || key[i] > bk)) {  // ascending e: strict > keeps lower id
+                bk = key[i];
+                bw = wl[i];
+                be = e;
+            }
+        }
+        for (int m = 32; m >= 1; m >>= 1) {
+            double ok_ = __shfl_xor(bk, m, 64);
+            double ow = __shfl_xor(bw, m, 64);
+            int oe = __shfl_xor(be, m, 64);
+            bool take = (oe != 0x7fffffff) &&
+                        (be == 0x7fffffff || ok_ > bk || (ok_ == bk && oe < be));
+            if (take) { bk = ok_; bw = ow; be = oe; }
+        }
+        if ((be & 63) == lane) taken |= 1u << (be >> 6);
+        if (lane == j) { my_e = be; my_wl = bw; }
+    }
+    // weights: softmax over the selected weight-logits (== full softmax
+    // restricted to the selection and renormalised)
+    double mx = (lane < k) ? my_wl : -DBL_MAX;
+    for (int m = 32; m >= 1; m >>= 1) mx = fmax(mx, __shfl_xor(mx, m, 64));
+    double ex = (lane < k) ? exp(my_wl - mx) : 0.0;
+    double sum = ex;
+    for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+    if (lane < k) {
+        idx_out[lane] = my_e;
+        w_out[lane] = (float)(ex / sum);
+        sel_e_out[lane] = my_e;
+    }
+}
+
+// One block per 64-token chunk, 16 waves.  Writes topk_idx / topk_w, the
+// chunk's per-expert token masks and counts.  A single-chunk batch (T <= 64)
+// also finishes the grouping here: counts, offsets, perm_pair, row_of_pair.
+__global__ __launch_bounds__(1024) void topk_group_kernel(
+    int T, int E, int k, const double* __restrict__ logits, const float* __restrict__ bias,
+    int bias_select_only, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    uint64_t* __restrict__ chunk_masks, int32_t* __restrict__ chunk_cnt,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm_pair, int32_t* __restrict__ row_of_pair)
+{
+    __shared__ unsigned long long mask[1024];
+    __shared__ int sel[kChunk * 32];
+    __shared__ int offs[1025];
+    __shared__ int wave_tot[17];
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int c = blockIdx.x, t0 = c * kChunk;
+    const int nt = min(kChunk, T - t0);
+    for (int e = tid; e < E; e += blockDim.x) mask[e] = 0ull;
+    __syncthreads();
+    for (int tl = wave; tl < nt; tl += 16) {
+        int t = t0 + tl;
+        wave_topk(E, k, logits + (size_t)t * E, bias, bias_select_only, sel + tl * 32,
+                  topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+    }
+    __syncthreads();
+    for (int i = tid; i < nt * k; i += blockDim.x) {
+        int tl = i / k, j = i - tl * k;
+        atomicOr(&mask[sel[tl * 32 + j]], 1ull << tl);
+    }
+    __syncthreads();
+    if (gridDim.x > 1) {
+        for (int e = tid; e < E; e += blockDim.x) {
+            chunk_masks[(size_t)c * E + e] = mask[e];
+            chunk_cnt[(size_t)c * E + e] = __popcll(mask[e]);
+        }
+        return;
+    }
+    // single chunk: finish the grouping in this block
+    int cnt = (tid < E) ? __popcll(mask[tid]) : 0;
+    int total;
+    int excl = block_exclusive_scan(cnt, wave_tot, &total);
+    if (tid < E) {
+        counts[tid] = cnt;
+        offsets[tid] = excl;
+        offs[tid] = excl;
+    }
+    if (tid == 0) offsets[E] = total;
+    __syncthreads();
+    for (int i = tid; i < nt * k; i += blockDim.x) {
+        int tl = i / k, j = i - tl * k;
+        int e = sel[tl * 32 + j];
+        int row = offs[e] + __popcll(mask[e] & ((1ull << tl) - 1ull));
+        int p = (t0 + tl) * k + j;
+        perm_pair[row] = p;
+        row_of_pair[p] = row;
+    }
+}
+
+// Multi-chunk grouping, step 2: per expert, prefix over chunks; then a
+// block-wide prefix over experts.  One block of 1024 threads (E <= 1024).
+__global__ __launch_bounds__(1024) void group_scan_kernel(
+    int nch, int E, int P, const int32_t* chunk_cnt, int32_t* chunk_base,  // may alias
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets)
+{
+    __shared__ int wave_tot[17];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        for (int c = 0; c < nch; ++c) {
+            int v = chunk_cnt[(size_t)c * E + e];
+            chunk_base[(size_t)c * E + e] = run;
+            run += v;
+        }
+    }
+    int total;
+    int excl = block_exclusive_scan(e < E ? run : 0, wave_tot, &total);
+    if (e < E) {
+        counts[e] = run;
+        offsets[e] = excl;
+    }
+    if (e == 0) offsets[E] = P;
+}
+
+// Multi-chunk grouping, step 3: each pair's row = expert offset + rows of the
+// expert in earlier chunks + earlier tokens of the same chunk (popcount).
+__global__ __launch_bounds__(256) void group_scatter_kernel(
+    int P, int E, int k, const int32_t* __restrict__ topk_idx,
+    const uint64_t* __restrict__ chunk_masks, const int32_t* __restrict__ chunk_base,
+    const int32_t* __restrict__ offsets, int32_t* __restrict__ perm_pair,
+    int32_t* __restrict__ row_of_pair)
+{
+    int p = blockIdx.x * 256 + threadIdx.x;
+    if (p >= P) return;
+    int t = p / k;
+    int e = topk_idx[p];
+    int c = t / kChunk, tl = t - c * kChunk;
+    size_t ce = (size_t)c * E + e;
+    int row = offsets[e] + chunk_base[ce] + __popcll(chunk_masks[ce] & ((1ull << tl) - 1ull));
+    perm_pair[row] = p;
+    row_of_pair[p] = row;
+}
+
+void launch_topk_group(int T, int E, int k, const double* logits, const float* bias,
+                       int bias_select_only, int32_t* topk_idx, float* topk_w,
+                       uint64_t* chunk_masks, int32_t* chunk_base, int32_t* counts,
+                       int32_t* offsets, int32_t* perm_pair, int32_t* row_of_pair,
+                       hipStream_t s)
+{
+    const int nch = (T + kChunk - 1) / kChunk;
+    // chunk_base doubles as the per-chunk count array before the scan
+    topk_group_kernel<<<dim3(nch), dim3(1024), 0, s>>>(T, E, k, logits, bias, bias_select_only,
+                                                       topk_idx, topk_w, chunk_masks, chunk_base,
+                                                       counts, offsets, perm_pair, row_of_pair);
+    if (nch > 1) {
+        const int P = T * k;
+        group_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(nch, E, P, chunk_base, chunk_base,
+                                                          counts, offsets);
+        group_scatter_kernel<<<dim3((P + 255) / 256), dim3(256), 0, s>>>(
+            P, E, k, topk_idx, chunk_masks, chunk_base, offsets, perm_pair, row_of_pair);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Active experts in ascending id (those with at least one token); the count
+// goes to active[E].
+__global__ __launch_bounds__(1024) void active_list_kernel(int E, const int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ active)
+{
+    __shared__ int wave_tot[17];
+    const int e = threadIdx.x;
+    int flag = (e < E) ? (offsets[e + 1] > offsets[e]) : 0;
+    int total;
+    int pos = block_exclusive_scan(flag, wave_tot, &total);
+    if (flag) active[pos] = e;
+    if (e == 0) active[E] = total;
+}
+
+void launch_active_list(int E, const int32_t* offsets, int32_t* active, hipStream_t s)
+{
+    active_list_kernel<<<dim3(1), dim3(1024), 0, s>>>(E, offsets, active);
+}
+
+}  // namespace k3
