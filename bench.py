@@ -1,0 +1,200 @@
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+One step = one pass of the whole layer (router, top-k, grouping, expert FFN on
+MXFP4 weights, combine) over one batch of synthetic tokens already resident
+in HBM.  The default workload is single-token greedy decode on the
+896-expert / top-16 layer (d_model 7168, d_ff 2048), a fresh seeded token per
+step (1000 distinct tokens, cycled).
+
+Prints one JSON line: throughput in tokens/s, the expert-FFN stage against the
+HBM roofline (active-expert bytes / the stage's average duration, timed with
+HIP events on the launch stream), and the fp64 oracle timed on the host cores
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
+MXFP4_PEAK_TFLOPS = 10100.0  # dense MXFP4 matrix peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="k3_decode_t1")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of host time for the oracle baseline (0 disables it)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step from a captured HIP graph instead of eager launches")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    import synthdata
+    import mxfp4_routed_expert_softmax_amd as k3
+
+    wl = synthdata.WORKLOADS[args.workload]
+    sh, T = wl.shape, wl.T
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {wl.name}: T={T} E={sh.E} k={sh.k} d={sh.d} f={sh.f} act={wl.act_mode}")
+
+    t0 = time.time()
+    experts = synthdata.upload_experts(sh, dev)
+    wr = torch.from_numpy(synthdata.router_weight(sh)).to(dev)
+    bias = torch.from_numpy(synthdata.zipf_bias(sh)).to(dev) if wl.zipf_bias else None
+    bias_mode = "logits" if wl.zipf_bias else "none"
+    # distinct seeded batches, resident in HBM before timing
+    nbatch = 1000 if T == 1 else max(1, min(8, 1000 // T))
+    xs = [torch.from_numpy(synthdata.tokens(sh, T, first=i * T)).to(dev) for i in range(nbatch)]
+    torch.cuda.synchronize()
+    log(f"inputs resident in {time.time() - t0:.1f}s ({nbatch} batches)")
+
+    fw = k3.Forward(xs[0], wr, experts, sh.k, bias, bias_mode, wl.act_mode)
+    stream = torch.cuda.current_stream()
+    route = fw.route
+
+    def step(i, ev=None):
+        fw.set_x(xs[i % nbatch])
+        fw.run_route()
+        if ev is not None:
+            ev[0].record(stream)
+        fw.run_ffn()
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    graph = None
+    if args.graph:
+        gx = xs[0].clone()
+        fw.set_x(gx)
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            fw.stream = s
+            fw()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            fw()
+        fw.stream = None
+        torch.cuda.synchronize()
+
+    # timed region: K steps; events bracket the expert-FFN stage of each step
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    if graph is None:
+        for i in range(args.steps):
+            step(i, evs[i])
+    else:
+        for i in range(args.steps):
+            gx.copy_(xs[i % nbatch], non_blocking=True)
+            graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = T * args.steps / elapsed
+
+    # bytes of the active experts, from this run's own counts (last step)
+    counts = route["counts"].cpu().numpy()
+    n_active = int((counts > 0).sum())
+    expert_bytes = n_active * sh.expert_bytes
+    act_bytes = 2 * T * sh.d * 4  # x read, y written
+    roofline = None
+    if graph is None:
+        ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        achieved = (expert_bytes + act_bytes) / (ffn_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "expert FFN stage (k3moe_ffn: gate/up GEMV + down GEMV + combine)",
+                    "bytes_per_launch": expert_bytes + act_bytes, "avg_ms": round(ffn_ms, 5)}
+    if wl.act_mode == "mxfp4" and roofline is not None:
+        flops = 2.0 * 3 * sh.d * sh.f * T * sh.k
+        roofline["mfma_frac"] = round(flops / (roofline["avg_ms"] * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS, 4)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(sh, wl, args.cpu_seconds)
+
+    out = {
+        "metric": "MoE-layer tokens/s at 1 MI355X (single-token decode, 896 experts, top-16)",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": T, "E": sh.E, "k": sh.k, "d_model": sh.d, "d_ff": sh.f,
+                   "activations": wl.act_mode, "weights": "MXFP4 (E2M1 codes + E8M0 block-32 scales)",
+                   "router_bias": bias_mode, "distinct_batches": nbatch,
+                   "launch": "hip graph replay" if graph is not None else "eager, one stream",
+                   "active_experts_last_step": n_active},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(sh, wl, budget_s):
+    """The fp64 oracle, as it stands, on the host cores: whole layer (router
+    over all experts, top-k, grouping, expert FFNs, combine) for as many
+    tokens of the workload as fit the time budget (at least one).  Expert
+    weights for the sampled tokens are generated before the clock starts."""
+    import oracle
+    import synthdata
+
+    wr = synthdata.router_weight(sh)
+    bias = synthdata.zipf_bias(sh) if wl.zipf_bias else None
+    bm = oracle.BIAS_LOGITS if wl.zipf_bias else oracle.BIAS_NONE
+    cache = {}
+    done, spent, tok = 0, 0.0, 0
+    while done == 0 or spent < budget_s:
+        x = synthdata.tokens(sh, 1, first=tok)
+        r = oracle.route(x, wr, sh.k, bias, bm)          # warm expert cache outside the clock
+        for e in r["topk_idx"][0]:
+            if int(e) not in cache:
+                cache[int(e)] = synthdata.expert(sh, int(e))
+        t0 = time.perf_counter()
+        r = oracle.route(x, wr, sh.k, bias, bm)
+        oracle.token_forward(x[0], r["topk_idx"][0], r["topk_w"][0], lambda e: cache[int(e)],
+                             act_mode=wl.act_mode)
+        spent += time.perf_counter() - t0
+        done += 1
+        tok += 1
+        if len(cache) > 256:
+            cache.clear()
+    return {"value": round(done / spent, 4), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} single tokens of {wl.name} (full layer per token, fp64), {spent:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

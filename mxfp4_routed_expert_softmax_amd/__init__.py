@@ -190,9 +190,11 @@ def k3moe_ffn(x, experts, route, act_mode="fp32", y=None, dbg=None, ws=None, str
 
 
 class Forward:
-    """k3moe_forward bound once to fixed buffers, so repeated calls (a decode
-    loop, a benchmark) cost one ctypes call each.  ``x`` may be rebound by
-    ``set_x`` to another tensor of the same shape."""
+    """The layer bound once to fixed buffers, so repeated calls (a decode loop,
+    a benchmark) cost one ctypes call each.  ``run_route`` / ``run_ffn`` issue
+    k3moe_route / k3moe_ffn, ``__call__`` issues k3moe_forward; all on the
+    current torch stream unless ``stream`` is given.  ``set_x`` rebinds the
+    activations to another tensor of the same shape."""
 
     def __init__(self, x, w_router, experts, k, bias=None, bias_mode="none", act_mode="fp32",
                  dbg=None, stream=None):
@@ -208,28 +210,39 @@ class Forward:
         self.route = alloc_route(T, E, k, x.device)
         self.y = torch.empty((T, d), dtype=torch.float32, device=x.device)
         self.ws = alloc_workspace(T, E, k, d, f, act_mode, x.device)
-        self._keep = (x, w_router, bias, experts, dbg)
+        self._keep = [x, w_router, bias, experts, dbg]
         self._dbg = _debug_struct(dbg)
+        self._dbgp = ctypes.byref(self._dbg) if self._dbg is not None else None
         self._x = _ptr(x)
-        self._args_tail = None
         self._bias_mode = _BIAS[bias_mode]
         self._act = _ACT[act_mode]
         self._wr, self._bias = _ptr(w_router), _ptr(bias)
+        r = self.route
+        self._r = [_ptr(r[n]) for n in ("topk_idx", "topk_w", "counts", "offsets", "perm_pair",
+                                        "row_of_pair")]
+        self._y, self._ws, self._wsn = _ptr(self.y), _ptr(self.ws), self.ws.numel()
         self.stream = stream
 
     def set_x(self, x):
         _need(x, torch.float32, (self.dims.T, self.dims.d_model), "x")
         self._x = _ptr(x)
-        self._keep = (x,) + self._keep[1:]
+        self._keep[0] = x
+
+    def run_route(self):
+        rc = _lib().k3moe_route(ctypes.byref(self.dims), self._x, self._wr, self._bias, self._bias_mode,
+                                *self._r, self._ws, self._wsn, _stream(self.stream))
+        _check(rc, "k3moe_route")
+
+    def run_ffn(self):
+        rc = _lib().k3moe_ffn(ctypes.byref(self.dims), self._x, ctypes.byref(self.experts), *self._r,
+                              self._act, self._y, self._dbgp, self._ws, self._wsn, _stream(self.stream))
+        _check(rc, "k3moe_ffn")
+        return self.y
 
     def __call__(self):
-        r = self.route
         rc = _lib().k3moe_forward(ctypes.byref(self.dims), self._x, self._wr, self._bias, self._bias_mode,
-                                  ctypes.byref(self.experts), self._act, _ptr(r["topk_idx"]),
-                                  _ptr(r["topk_w"]), _ptr(r["counts"]), _ptr(r["offsets"]),
-                                  _ptr(r["perm_pair"]), _ptr(r["row_of_pair"]), _ptr(self.y),
-                                  ctypes.byref(self._dbg) if self._dbg is not None else None,
-                                  _ptr(self.ws), self.ws.numel(), _stream(self.stream))
+                                  ctypes.byref(self.experts), self._act, *self._r, self._y, self._dbgp,
+                                  self._ws, self._wsn, _stream(self.stream))
         _check(rc, "k3moe_forward")
         return self.y
 

@@ -9,19 +9,68 @@
 // MXFP4 computation).  Each active expert's rows are read once per step and
 // applied to every token routed to it.
 //
-// Work mapping: a group of G lanes owns a few weight rows and splits the
-// reduction axis; every lane streams one 32-element MX block (16 code bytes,
-// one 128-bit load, plus its scale byte) per row per step, so a group reads
-// G*16 contiguous bytes of each row per step.  The gfx950 scaled convert
-// turns two codes into two fp32 values with the block's power-of-two scale
-// applied, exactly.  Partial sums are reduced across the group by shuffles.
+// Work mapping (both GEMVs): the reduction axis is split over the lanes of a
+// workgroup, one 32-element MX block per lane (BPL blocks if the axis is
+// longer than the group), so each lane keeps its slice of the activation in
+// registers for the whole kernel and no activation is re-read per row.  A
+// wave then streams rows: per row a lane loads 16 code bytes (one 128-bit
+// load; 64 lanes read 1 KB of the row contiguously) and one scale byte, and
+// the gfx950 scaled convert turns two codes at a time into fp32 with the
+// block's power-of-two scale applied exactly.  Sixteen rows are issued
+// together, then reduced across the wave with a transposed shuffle
+// reduction (17 swizzles for 16 rows) and, when several waves share a row,
+// across waves through LDS in a fixed order -- deterministic sums.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace k3 {
 
+// xor-swizzle inside 32-lane halves (ds_swizzle bitmask mode, no LDS access)
+template <int M>
+__device__ __forceinline__ float swz_xor(float v)
+{
+    static_assert(M > 0 && M < 32, "swizzle masks reach 31");
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1F));
+}
+
+__device__ __forceinline__ float xor32(float v)
+{
+    const int lane = threadIdx.x & 63;
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(v)));
+}
+
+// 16 partial sums per lane -> lane l holds the wave-wide sum of acc[l & 15].
+// Step by step the lane whose bit is set keeps the upper half and sends the
+// lower half to its partner; the order of additions is fixed.
+__device__ __forceinline__ float wave_transpose_sum16(const float (&acc)[16])
+{
+    const int lane = threadIdx.x & 63;
+    float a8[8], a4[4], a2[2];
+    const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float keep = b3 ? acc[i + 8] : acc[i], send = b3 ? acc[i] : acc[i + 8];
+        a8[i] = keep + swz_xor<8>(send);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float keep = b2 ? a8[i + 4] : a8[i], send = b2 ? a8[i] : a8[i + 4];
+        a4[i] = keep + swz_xor<4>(send);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        float keep = b1 ? a4[i + 2] : a4[i], send = b1 ? a4[i] : a4[i + 2];
+        a2[i] = keep + swz_xor<2>(send);
+    }
+    float keep = b0 ? a2[1] : a2[0], send = b0 ? a2[0] : a2[1];
+    float s = keep + swz_xor<1>(send);
+    s += swz_xor<16>(s);
+    s += xor32(s);
+    return s;
+}
+
 // Which expert does this block's slot serve?  Either the slot-th entry of the
-// active list, or (no list) slot = a sorted row that must head its expert's
+// active list, or (no list) slot = a grouped row that must head its expert's
 // segment.  Returns false for idle slots.
 __device__ __forceinline__ bool slot_expert(const FfnArgs& a, int slot, int& e, int& r_beg, int& n_e)
 {
@@ -38,133 +87,267 @@ __device__ __forceinline__ bool slot_expert(const FfnArgs& a, int slot, int& e, 
     return n_e > 0;
 }
 
-// ---------------------------------------------------------------------------
-// gate/up: block = 8 groups of 32 lanes; group g owns gate rows r0..r0+3 and
-// the same up rows.  h[row][r] = silu(g_r) * u_r for every token row of the
-// expert, TCH tokens per pass over the weights.
-template <int TCH>
-__global__ __launch_bounds__(256) void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h)
+// Load the lane's activation slice (BPL blocks of 32) of one row, zeros past
+// the end of the reduction axis.
+template <int BPL>
+__device__ __forceinline__ void load_act(const float* row, int blk0, int stride_blk, int nb,
+                                         float (&xr)[BPL][32])
 {
-    constexpr int R = 4;
-    int e, r_beg, n_e;
-    if (!slot_expert(a, blockIdx.y, e, r_beg, n_e)) return;
-    const int lane = threadIdx.x & 31, grp = threadIdx.x >> 5;
-    const int r0 = (blockIdx.x * 8 + grp) * R;
-    if (r0 >= a.f) return;
-    const int d = a.d, nb = d >> 5;
-    const size_t crow = (size_t)(d >> 1), srow = (size_t)nb;
-    const size_t wrow0 = (size_t)e * a.f + r0;
-    const uint8_t* gcp = a.gc + wrow0 * crow;
-    const uint8_t* ucp = a.uc + wrow0 * crow;
-    const uint8_t* gsp = a.gs + wrow0 * srow;
-    const uint8_t* usp = a.us + wrow0 * srow;
-
-    for (int t0 = 0; t0 < n_e; t0 += TCH) {
-        const float* xr[TCH];
 #pragma unroll
-        for (int tt = 0; tt < TCH; ++tt) {
-            int m = min(t0 + tt, n_e - 1);
-            int tok = a.perm_pair[r_beg + m] / a.k;
-            xr[tt] = a.x + (size_t)tok * d;
-        }
-        float ag[TCH][R], au[TCH][R];
+    for (int b = 0; b < BPL; ++b) {
+        int blk = blk0 + b * stride_blk;
+        if (blk < nb) {
+            load32f(row + (size_t)blk * 32, xr[b]);
+        } else {
 #pragma unroll
-        for (int tt = 0; tt < TCH; ++tt)
-#pragma unroll
-            for (int i = 0; i < R; ++i) { ag[tt][i] = 0.f; au[tt][i] = 0.f; }
-
-        for (int blk = lane; blk < nb; blk += 32) {
-            uint4 qg[R], qu[R];
-            float sg[R], su[R];
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                qg[i] = ldg16(gcp + i * crow + (size_t)blk * 16);
-                qu[i] = ldg16(ucp + i * crow + (size_t)blk * 16);
-                sg[i] = e8m0_f32(gsp[i * srow + blk]);
-                su[i] = e8m0_f32(usp[i * srow + blk]);
-            }
-#pragma unroll
-            for (int tt = 0; tt < TCH; ++tt) {
-                if (t0 + tt < n_e) {
-                    float xs[32];
-                    load32f(xr[tt] + (size_t)blk * 32, xs);
-#pragma unroll
-                    for (int i = 0; i < R; ++i) {
-                        ag[tt][i] = dot32_fp4(qg[i], sg[i], xs, ag[tt][i]);
-                        au[tt][i] = dot32_fp4(qu[i], su[i], xs, au[tt][i]);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int tt = 0; tt < TCH; ++tt) {
-            if (t0 + tt >= n_e) break;
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                float g = ag[tt][i], u = au[tt][i];
-#pragma unroll
-                for (int m = 16; m >= 1; m >>= 1) {
-                    g += shfl_xor(g, m, 32);
-                    u += shfl_xor(u, m, 32);
-                }
-                if (lane == i) h[(size_t)(r_beg + t0 + tt) * a.f + r0 + i] = silu_f32(g) * u;
-            }
+            for (int i = 0; i < 32; ++i) xr[b][i] = 0.f;
         }
     }
 }
 
-// ---------------------------------------------------------------------------
-// down: block = 16 groups of 16 lanes; group g owns down rows c0..c0+7.
-// o[row][c] = Wd_e[c,:] . h[row] for every token row of the expert.
-template <int TCH>
-__global__ __launch_bounds__(256) void down_gemv_kernel(FfnArgs a, const float* __restrict__ h,
-                                                        float* __restrict__ o)
+// Make the compiler treat v as redefined here: stops loop-invariant code
+// motion from hoisting the decode of a weight block out of a token loop
+// (which would keep every decoded value of a batch live at once).
+__device__ __forceinline__ void opaque(uint4& v)
 {
-    constexpr int R = 8;
-    int e, r_beg, n_e;
-    if (!slot_expert(a, blockIdx.y, e, r_beg, n_e)) return;
-    const int lane = threadIdx.x & 15, grp = threadIdx.x >> 4;
-    const int c0 = (blockIdx.x * 16 + grp) * R;
-    if (c0 >= a.d) return;
-    const int f = a.f, nb = f >> 5;
-    const size_t crow = (size_t)(f >> 1), srow = (size_t)nb;
-    const size_t wrow0 = (size_t)e * a.d + c0;
-    const uint8_t* dcp = a.dc + wrow0 * crow;
-    const uint8_t* dsp = a.ds + wrow0 * srow;
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
 
-    for (int t0 = 0; t0 < n_e; t0 += TCH) {
-        float acc[TCH][R];
+// acc[tt] += (one 32-element MX block: 16 code bytes q, scale sc) . xs[tt][0..31]
+// for TCH token rows; every code pair is decoded once and used by all rows.
+template <int TCH>
+__device__ __forceinline__ void dot32_multi(uint4 q, float sc, const float (&xs)[TCH][32], float (&acc)[TCH])
+{
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-        for (int tt = 0; tt < TCH; ++tt)
-#pragma unroll
-            for (int i = 0; i < R; ++i) acc[tt][i] = 0.f;
-        for (int blk = lane; blk < nb; blk += 16) {
-            uint4 q[R];
-            float sc[R];
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                q[i] = ldg16(dcp + i * crow + (size_t)blk * 16);
-                sc[i] = e8m0_f32(dsp[i * srow + blk]);
-            }
-#pragma unroll
-            for (int tt = 0; tt < TCH; ++tt) {
-                if (t0 + tt < n_e) {
-                    float hs[32];
-                    load32f(h + (size_t)(r_beg + t0 + tt) * f + (size_t)blk * 32, hs);
-#pragma unroll
-                    for (int i = 0; i < R; ++i) acc[tt][i] = dot32_fp4(q[i], sc[i], hs, acc[tt][i]);
-                }
-            }
-        }
+    for (int k = 0; k < 4; ++k) {
+        f32x2 p0 = fp4x2_scaled<0>(w[k], sc);
+        f32x2 p1 = fp4x2_scaled<1>(w[k], sc);
+        f32x2 p2 = fp4x2_scaled<2>(w[k], sc);
+        f32x2 p3 = fp4x2_scaled<3>(w[k], sc);
 #pragma unroll
         for (int tt = 0; tt < TCH; ++tt) {
-            if (t0 + tt >= n_e) break;
+            const float* x = xs[tt] + 8 * k;
+            float s = acc[tt];
+            s = __builtin_fmaf(p0.x, x[0], s);
+            s = __builtin_fmaf(p0.y, x[1], s);
+            s = __builtin_fmaf(p1.x, x[2], s);
+            s = __builtin_fmaf(p1.y, x[3], s);
+            s = __builtin_fmaf(p2.x, x[4], s);
+            s = __builtin_fmaf(p2.y, x[5], s);
+            s = __builtin_fmaf(p3.x, x[6], s);
+            s = __builtin_fmaf(p3.y, x[7], s);
+            acc[tt] = s;
+        }
+    }
+}
+
+// Weight rows are read through a buffer resource on the block's (uniform)
+// matrix base: one 32-bit lane offset serves every row (the row offset is a
+// scalar), and a lane whose offset is >= 2^31 reads zeros without touching
+// memory -- the lanes past the end of the reduction axis.
+constexpr uint32_t kOff = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const uint8_t* base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 ld_codes(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, (int)soff, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint32_t ld_scale(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b8(r, voff, (int)soff, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Partial sums of a batch: acc[tt * R + i] = row i of the batch for token tt,
+// R = 16 / TCH rows per batch, so one transposed reduction serves the batch.
+
+// gate/up.  Block = 4 waves; the 256 lanes split the d axis (lane = block,
+// BPL blocks per lane).  The block walks kGuRows row pairs of one expert in
+// batches of R rows (R/2 gate rows + the same R/2 up rows); each wave reduces
+// a batch with one transposed reduction and parks the sums in LDS; one
+// fixed-order cross-wave sum per token pass gives g and u, and
+// h = silu(g) * u is written per token row of the expert.
+constexpr int kGuRows = 32;  // row pairs per block
+
+template <int TCH, int BPL>
+__global__ __launch_bounds__(256) void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h)
+{
+    constexpr int R = 16 / TCH, HALF = R / 2;
+    __shared__ float part[TCH][4][kGuRows * 2];  // [tt][wave][gate rows | up rows]
+    int e, r_beg, n_e;
+    if (!slot_expert(a, blockIdx.y, e, r_beg, n_e)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r0 = blockIdx.x * kGuRows;
+    const int d = a.d, nb = d >> 5;
+    const size_t crow = (size_t)(d >> 1), srow = (size_t)nb;
+    const size_t wrow0 = (size_t)e * a.f + r0;
+    const int npairs = min(kGuRows, a.f - r0);  // multiple of 8 (f % 32 == 0)
+    const __amdgpu_buffer_rsrc_t rg = weight_rsrc(a.gc + wrow0 * crow);
+    const __amdgpu_buffer_rsrc_t ru = weight_rsrc(a.uc + wrow0 * crow);
+    const __amdgpu_buffer_rsrc_t rgs = weight_rsrc(a.gs + wrow0 * srow);
+    const __amdgpu_buffer_rsrc_t rus = weight_rsrc(a.us + wrow0 * srow);
+    uint32_t coff[BPL], soffl[BPL];
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+        const int blk = tid + 256 * b;
+        coff[b] = blk < nb ? (uint32_t)blk * 16u : kOff;
+        soffl[b] = blk < nb ? (uint32_t)blk : kOff;
+    }
+
+    for (int t0 = 0; t0 < n_e; t0 += TCH) {
+        float xr[BPL][TCH][32];
+#pragma unroll
+        for (int tt = 0; tt < TCH; ++tt) {
+            int m = min(t0 + tt, n_e - 1);
+            int tok = a.perm_pair[r_beg + m] / a.k;
+            float tmp[BPL][32];
+            load_act<BPL>(a.x + (size_t)tok * d, tid, 256, nb, tmp);
+#pragma unroll
+            for (int b = 0; b < BPL; ++b)
+#pragma unroll
+                for (int i = 0; i < 32; ++i) xr[b][tt][i] = tmp[b][i];
+        }
+        for (int pb = 0; pb < npairs; pb += HALF) {
+            uint4 q[R][BPL];
+            uint32_t sb[R][BPL];
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                float v = acc[tt][i];
+                const uint32_t row = (uint32_t)(pb + (i % HALF));
 #pragma unroll
-                for (int m = 8; m >= 1; m >>= 1) v += shfl_xor(v, m, 16);
-                if (lane == i) o[(size_t)(r_beg + t0 + tt) * a.d + c0 + i] = v;
+                for (int b = 0; b < BPL; ++b) {
+                    q[i][b] = ld_codes(i < HALF ? rg : ru, coff[b], row * (uint32_t)crow);
+                    sb[i][b] = ld_scale(i < HALF ? rgs : rus, soffl[b], row * (uint32_t)srow);
+                }
+            }
+            float acc[16];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                float s[TCH];
+#pragma unroll
+                for (int tt = 0; tt < TCH; ++tt) s[tt] = 0.f;
+#pragma unroll
+                for (int b = 0; b < BPL; ++b) dot32_multi<TCH>(q[i][b], e8m0_f32(sb[i][b]), xr[b], s);
+#pragma unroll
+                for (int tt = 0; tt < TCH; ++tt) acc[tt * R + i] = s[tt];
+            }
+            const float v = wave_transpose_sum16(acc);
+            if (lane < 16) {
+                const int tt = lane / R, i = lane % R;
+                // gate row pb + i -> slot pb + i; up row pb + i - HALF -> kGuRows + pb + i - HALF
+                part[tt][wave][i < HALF ? pb + i : kGuRows + pb + i - HALF] = v;
+            }
+        }
+        __syncthreads();
+        // fixed-order cross-wave sum; thread (tt, r) finishes row r of token tt
+        for (int i = tid; i < TCH * npairs; i += 256) {
+            const int tt = i / npairs, r = i - tt * npairs;
+            if (t0 + tt < n_e) {
+                float g = 0.f, u = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    g += part[tt][w][r];
+                    u += part[tt][w][kGuRows + r];
+                }
+                h[(size_t)(r_beg + t0 + tt) * a.f + r0 + r] = silu_f32(g) * u;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// down.  Block = 4 waves; NK waves split the f axis (one block per lane, BPL
+// per lane beyond 64*NK blocks), 4/NK teams of waves take different rows.
+// Each team owns kDnRows rows of the expert, walked in batches of R rows;
+// the weights of a batch are loaded once and applied to every token pass.
+constexpr int kDnRows = 16;  // rows per team
+
+template <int TCH, int NK, int BPL>
+__global__ __launch_bounds__(256) void down_gemv_kernel(FfnArgs a, const float* __restrict__ hbuf,
+                                                        float* __restrict__ o)
+{
+    constexpr int TEAMS = 4 / NK, R = 16 / TCH;
+    __shared__ float part[NK > 1 ? 4 : 1][16];
+    int e, r_beg, n_e;
+    if (!slot_expert(a, blockIdx.y, e, r_beg, n_e)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int team = wave / NK, kw = wave % NK;
+    const int kl = kw * 64 + lane;  // lane index along the f axis
+    const int c0 = (blockIdx.x * TEAMS + team) * kDnRows;
+    const int f = a.f, nb = f >> 5;
+    const size_t crow = (size_t)(f >> 1), srow = (size_t)nb;
+    const bool live = c0 < a.d;  // d % 16 == 0: a team's rows are all in or all out
+    const size_t wrow0 = (size_t)e * a.d + (live ? c0 : 0);
+    const __amdgpu_buffer_rsrc_t rd = weight_rsrc(a.dc + wrow0 * crow);
+    const __amdgpu_buffer_rsrc_t rds = weight_rsrc(a.ds + wrow0 * srow);
+    uint32_t coff[BPL], soffl[BPL];
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+        const int blk = kl + 64 * NK * b;
+        coff[b] = blk < nb ? (uint32_t)blk * 16u : kOff;
+        soffl[b] = blk < nb ? (uint32_t)blk : kOff;
+    }
+
+    for (int rb = 0; rb < kDnRows; rb += R) {
+        uint4 q[R][BPL];
+        uint32_t sb[R][BPL];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+#pragma unroll
+            for (int b = 0; b < BPL; ++b) {
+                q[i][b] = ld_codes(rd, coff[b], (uint32_t)(rb + i) * (uint32_t)crow);
+                sb[i][b] = ld_scale(rds, soffl[b], (uint32_t)(rb + i) * (uint32_t)srow);
+            }
+        }
+        for (int t0 = 0; t0 < n_e; t0 += TCH) {
+            float hr[BPL][TCH][32];
+#pragma unroll
+            for (int tt = 0; tt < TCH; ++tt) {
+                int m = min(t0 + tt, n_e - 1);
+                float tmp[BPL][32];
+                load_act<BPL>(hbuf + (size_t)(r_beg + m) * f, kl, 64 * NK, nb, tmp);
+#pragma unroll
+                for (int b = 0; b < BPL; ++b)
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) hr[b][tt][i] = tmp[b][i];
+            }
+            float acc[16];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                float s[TCH];
+#pragma unroll
+                for (int tt = 0; tt < TCH; ++tt) s[tt] = 0.f;
+#pragma unroll
+                for (int b = 0; b < BPL; ++b) {
+                    uint4 qq = q[i][b];
+                    opaque(qq);
+                    dot32_multi<TCH>(qq, e8m0_f32(sb[i][b]), hr[b], s);
+                }
+#pragma unroll
+                for (int tt = 0; tt < TCH; ++tt) acc[tt * R + i] = s[tt];
+            }
+            const float v = wave_transpose_sum16(acc);
+            const int tt = (lane & 15) / R, i = (lane & 15) % R;
+            if (NK == 1) {
+                if (live && lane < 16 && t0 + tt < n_e)
+                    o[(size_t)(r_beg + t0 + tt) * a.d + c0 + rb + i] = v;
+            } else {
+                if (lane < 16) part[wave][lane] = v;
+                __syncthreads();
+                if (kw == 0 && lane < 16 && live && t0 + tt < n_e) {
+                    float sum = 0.f;
+#pragma unroll
+                    for (int w = 0; w < NK; ++w) sum += part[team * NK + w][lane];
+                    o[(size_t)(r_beg + t0 + tt) * a.d + c0 + rb + i] = sum;
+                }
+                __syncthreads();
             }
         }
     }
@@ -192,22 +375,58 @@ __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a, const float* __
     reinterpret_cast<float4*>(y + (size_t)t * a.d)[c4] = acc;
 }
 
+// ---------------------------------------------------------------------------
+static int tokens_per_pass(const FfnArgs& a) { return a.T == 1 ? 1 : 2; }
+
+template <int TCH>
+static void gateup_dispatch(const FfnArgs& a, float* h, hipStream_t s)
+{
+    const int nb = a.d / 32;
+    dim3 grid((a.f + kGuRows - 1) / kGuRows, a.nslots);
+    if (nb <= 256)
+        gateup_gemv_kernel<TCH, 1><<<grid, dim3(256), 0, s>>>(a, h);
+    else
+        gateup_gemv_kernel<TCH, 2><<<grid, dim3(256), 0, s>>>(a, h);  // d <= 16384 (checked)
+}
+
 void launch_gateup_gemv(const FfnArgs& a, float* h, hipStream_t s)
 {
-    dim3 grid((a.f + 31) / 32, a.nslots);
-    if (a.T == 1)
-        gateup_gemv_kernel<1><<<grid, dim3(256), 0, s>>>(a, h);
+    if (tokens_per_pass(a) == 1)
+        gateup_dispatch<1>(a, h, s);
     else
-        gateup_gemv_kernel<4><<<grid, dim3(256), 0, s>>>(a, h);
+        gateup_dispatch<2>(a, h, s);
+}
+
+template <int TCH, int NK>
+static void down_dispatch_nk(const FfnArgs& a, const float* h, float* o, hipStream_t s)
+{
+    const int nb = a.f / 32;
+    constexpr int TEAMS = 4 / NK;
+    dim3 grid((a.d + TEAMS * kDnRows - 1) / (TEAMS * kDnRows), a.nslots);
+    if (nb <= 64 * NK)
+        down_gemv_kernel<TCH, NK, 1><<<grid, dim3(256), 0, s>>>(a, h, o);
+    else
+        down_gemv_kernel<TCH, NK, 2><<<grid, dim3(256), 0, s>>>(a, h, o);  // f <= 16384 (checked)
+}
+
+template <int TCH>
+static void down_dispatch(const FfnArgs& a, const float* h, float* o, hipStream_t s)
+{
+    const int nb = a.f / 32;
+    if (nb <= 64)
+        down_dispatch_nk<TCH, 1>(a, h, o, s);
+    else if (nb <= 128)
+        down_dispatch_nk<TCH, 2>(a, h, o, s);
+    else
+        down_dispatch_nk<TCH, 4>(a, h, o, s);
 }
 
 void launch_down_gemv(const FfnArgs& a, const float* h, float* o, hipStream_t s)
 {
-    dim3 grid((a.d + 127) / 128, a.nslots);
-    if (a.T == 1)
-        down_gemv_kernel<1><<<grid, dim3(256), 0, s>>>(a, h, o);
+    if (tokens_per_pass(a) == 1)
+        down_dispatch<1>(a, h, o, s);
     else
-        down_gemv_kernel<4><<<grid, dim3(256), 0, s>>>(a, h, o);
+        down_dispatch<2>(a, h, o, s);
 }
 
 void launch_combine(const FfnArgs& a, const float* o, float* y, hipStream_t s)

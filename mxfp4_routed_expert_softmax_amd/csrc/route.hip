@@ -17,33 +17,53 @@
 namespace k3 {
 
 // ---------------------------------------------------------------------------
-// Router logits, small T: one wave per expert row, every token of the batch
-// accumulated while the row streams through once.  fp32 x fp32 products are
-// exact in fp64; the sums are fp64.
+// Router logits, small T: one 256-thread block per expert row; the threads
+// split d (float4 per thread per step, all of a thread's loads in flight at
+// once), every token of the batch accumulated while the row streams through.
+// fp32 x fp32 products are exact in fp64; the sums are fp64, reduced in a
+// fixed order (wave shuffles, then the four waves through LDS).
 constexpr int kGemvTok = 8;
+constexpr int kRouterPerThread = 8;  // float4 steps per thread: d <= 8192 in one pass
+
+__device__ __forceinline__ double shfl_xor_d(double v, int m)
+{
+    return __shfl_xor(v, m, 64);
+}
 
 __global__ __launch_bounds__(256) void router_gemv_kernel(
     int T, int E, int d, const float* __restrict__ x, const float* __restrict__ wr,
     const float* __restrict__ bias, int bias_in_logits, double* __restrict__ logits)
 {
-    const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= E) return;
+    __shared__ double part[kGemvTok][4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int e = blockIdx.x;
     const float4* w4 = reinterpret_cast<const float4*>(wr + (size_t)e * d);
     const int n4 = d >> 2;
     double acc[kGemvTok];
 #pragma unroll
     for (int t = 0; t < kGemvTok; ++t) acc[t] = 0.0;
-    for (int i = lane; i < n4; i += 64) {
-        float4 w = w4[i];
+    for (int base = 0; base < n4; base += 256 * kRouterPerThread) {
+        float4 w[kRouterPerThread];
+#pragma unroll
+        for (int j = 0; j < kRouterPerThread; ++j) {
+            int i = base + tid + 256 * j;
+            w[j] = (i < n4) ? w4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
         for (int t = 0; t < kGemvTok; ++t) {
             if (t < T) {
-                float4 v = reinterpret_cast<const float4*>(x + (size_t)t * d)[i];
-                acc[t] = fma((double)w.x, (double)v.x, acc[t]);
-                acc[t] = fma((double)w.y, (double)v.y, acc[t]);
-                acc[t] = fma((double)w.z, (double)v.z, acc[t]);
-                acc[t] = fma((double)w.w, (double)v.w, acc[t]);
+                const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)t * d);
+#pragma unroll
+                for (int j = 0; j < kRouterPerThread; ++j) {
+                    int i = base + tid + 256 * j;
+                    if (i < n4) {
+                        float4 v = x4[i];
+                        acc[t] = fma((double)w[j].x, (double)v.x, acc[t]);
+                        acc[t] = fma((double)w[j].y, (double)v.y, acc[t]);
+                        acc[t] = fma((double)w[j].z, (double)v.z, acc[t]);
+                        acc[t] = fma((double)w[j].w, (double)v.w, acc[t]);
+                    }
+                }
             }
         }
     }
@@ -51,12 +71,15 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(
     for (int t = 0; t < kGemvTok; ++t) {
         if (t < T) {
             double v = acc[t];
-            for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-            if (lane == 0) {
-                if (bias_in_logits) v += (double)bias[e];
-                logits[(size_t)t * E + e] = v;
-            }
+            for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_d(v, m);
+            if (lane == 0) part[t][wave] = v;
         }
+    }
+    __syncthreads();
+    if (tid < T) {
+        double v = ((part[tid][0] + part[tid][1]) + part[tid][2]) + part[tid][3];
+        if (bias_in_logits) v += (double)bias[e];
+        logits[(size_t)tid * E + e] = v;
     }
 }
 
@@ -122,8 +145,8 @@ void launch_router_logits(int T, int E, int d, const float* x, const float* wr,
                           hipStream_t s)
 {
     if (T <= kGemvTok) {
-        router_gemv_kernel<<<dim3((E + 3) / 4), dim3(256), 0, s>>>(T, E, d, x, wr, bias,
-                                                                   bias_in_logits, logits);
+        router_gemv_kernel<<<dim3(E), dim3(256), 0, s>>>(T, E, d, x, wr, bias, bias_in_logits,
+                                                         logits);
     } else {
         router_gemm_kernel<<<dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s>>>(
             T, E, d, x, wr, bias, bias_in_logits, logits);
@@ -160,54 +183,90 @@ __device__ int block_exclusive_scan(int v, int* wave_tot, int* total)
 
 // Top-k of one token held by one wave: lane l owns experts l, l+64, ...
 // (E <= 1024 -> at most 16 per lane).  k rounds of a wave-wide
-// (key max, index min) reduction; the winning lane retires its entry.
+// (key max, index min) reduction; the winning lane retires its entry.  The
+// weight logits of the k winners are read back at the end (they equal the
+// keys unless the bias steers the selection only).
 constexpr int kMaxPerLane = 16;
+
+template <int M>
+__device__ __forceinline__ int swz_i(int v)
+{
+    return __builtin_amdgcn_ds_swizzle(v, (M << 10) | 0x1F);
+}
+
+__device__ __forceinline__ int bperm_i(int v, int src_lane)
+{
+    return __builtin_amdgcn_ds_bpermute(src_lane << 2, v);
+}
+
+template <int M>
+__device__ __forceinline__ void argmax_step(double& bk, int& be)
+{
+    const int lane = threadIdx.x & 63;
+    int lo = __double2loint(bk), hi = __double2hiint(bk);
+    int olo, ohi, oe;
+    if (M < 32) {
+        olo = swz_i<M>(lo);
+        ohi = swz_i<M>(hi);
+        oe = swz_i<M>(be);
+    } else {
+        olo = bperm_i(lo, lane ^ 32);
+        ohi = bperm_i(hi, lane ^ 32);
+        oe = bperm_i(be, lane ^ 32);
+    }
+    double ok = __hiloint2double(ohi, olo);
+    bool take = (oe != 0x7fffffff) && (be == 0x7fffffff || ok > bk || (ok == bk && oe < be));
+    if (take) {
+        bk = ok;
+        be = oe;
+    }
+}
 
 __device__ void wave_topk(int E, int k, const double* __restrict__ lrow,
                           const float* __restrict__ bias, int bias_select_only,
                           int* sel_e_out, int32_t* idx_out, float* w_out)
 {
     const int lane = threadIdx.x & 63;
-    double key[kMaxPerLane], wl[kMaxPerLane];
+    double key[kMaxPerLane];
+    uint32_t taken = 0;
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
         int e = lane + 64 * i;
-        double l = (e < E) ? lrow[e] : -DBL_MAX;
-        wl[i] = l;
-        key[i] = (e < E && bias_select_only) ? l + (double)bias[e] : l;
+        if (e < E) {
+            double l = lrow[e];
+            key[i] = bias_select_only ? l + (double)bias[e] : l;
+        } else {
+            key[i] = 0.0;
+            taken |= 1u << i;
+        }
     }
-    uint32_t taken = 0;
     int my_e = 0;
-    double my_wl = 0.0;
     for (int j = 0; j < k; ++j) {
-        double bk = 0.0, bw = 0.0;
+        double bk = 0.0;
         int be = 0x7fffffff;
 #pragma unroll
         for (int i = 0; i < kMaxPerLane; ++i) {
-            int e = lane + 64 * i;
-            bool ok = (e < E) && !((taken >> i) & 1u);
-            if (ok && (be == 0x7fffffff || key[i] > bk)) {  // ascending e: strict > keeps lower id
+            // ascending expert id inside the lane: strict > keeps the lower id
+            if (!((taken >> i) & 1u) && (be == 0x7fffffff || key[i] > bk)) {
                 bk = key[i];
-                bw = wl[i];
-                be = e;
+                be = lane + 64 * i;
             }
         }
-        for (int m = 32; m >= 1; m >>= 1) {
-            double ok_ = __shfl_xor(bk, m, 64);
-            double ow = __shfl_xor(bw, m, 64);
-            int oe = __shfl_xor(be, m, 64);
-            bool take = (oe != 0x7fffffff) &&
-                        (be == 0x7fffffff || ok_ > bk || (ok_ == bk && oe < be));
-            if (take) { bk = ok_; bw = ow; be = oe; }
-        }
+        argmax_step<1>(bk, be);
+        argmax_step<2>(bk, be);
+        argmax_step<4>(bk, be);
+        argmax_step<8>(bk, be);
+        argmax_step<16>(bk, be);
+        argmax_step<32>(bk, be);
         if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        if (lane == j) { my_e = be; my_wl = bw; }
+        if (lane == j) my_e = be;
     }
-    // weights: softmax over the selected weight-logits (== full softmax
+    // weights: softmax over the selected weight-logits (== the full softmax
     // restricted to the selection and renormalised)
-    double mx = (lane < k) ? my_wl : -DBL_MAX;
+    double wl = (lane < k) ? lrow[my_e] : 0.0;
+    double mx = (lane < k) ? wl : -DBL_MAX;
     for (int m = 32; m >= 1; m >>= 1) mx = fmax(mx, __shfl_xor(mx, m, 64));
-    double ex = (lane < k) ? exp(my_wl - mx) : 0.0;
+    double ex = (lane < k) ? exp(wl - mx) : 0.0;
     double sum = ex;
     for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
     if (lane < k) {
