@@ -29,6 +29,8 @@ FLAGS = [
     # keep fp32 denormals (the MX decode and quantiser rely on exact values)
     "-fno-gpu-flush-denormals-to-zero",
     "-fno-fast-math",
+    # a missing definition must fail the link, not the first dlopen
+    "-Wl,-z,defs",
 ]
 
 

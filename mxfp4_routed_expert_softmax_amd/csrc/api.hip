@@ -200,7 +200,11 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
     a.offsets = offsets;
     a.perm_pair = perm_pair;
     a.row_of_pair = row_of_pair;
-    if (a.P <= a.E) {
+    const bool pair_path = act_mode == K3MOE_ACT_FP32 && use_pair_path(a);
+    if (pair_path) {
+        a.active = nullptr;  // slots are pairs
+        a.nslots = a.P;
+    } else if (a.P <= a.E) {
         // few pairs: a slot per grouped row, the segment heads do the work
         a.active = nullptr;
         a.nslots = a.P;
@@ -214,8 +218,12 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
         float* h = reinterpret_cast<float*>(ws + L.h);
         float* o = reinterpret_cast<float*>(ws + L.o);
         launch_gateup_gemv(a, h, s);
-        launch_down_gemv(a, h, o, s);
-        launch_combine(a, o, y, s);
+        if (pair_path) {
+            launch_down_gather(a, h, y, s);
+        } else {
+            launch_down_gemv(a, h, o, s);
+            launch_combine(a, o, y, s);
+        }
     } else {
         uint8_t* xqc = reinterpret_cast<uint8_t*>(ws + L.xq_codes);
         uint8_t* xqs = reinterpret_cast<uint8_t*>(ws + L.xq_scales);

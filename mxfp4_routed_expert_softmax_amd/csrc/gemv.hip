@@ -176,13 +176,21 @@ __device__ __forceinline__ uint32_t ld_scale(__amdgpu_buffer_rsrc_t r, uint32_t 
 // h = silu(g) * u is written per token row of the expert.
 constexpr int kGuRows = 32;  // row pairs per block
 
-template <int TCH, int BPL>
+// PAIR: the pair-major variant for small batches -- block y serves pair
+// p = t*k + j alone (expert topk_idx[p], token t, h row p), no grouping.
+template <int TCH, int BPL, bool PAIR>
 __global__ __launch_bounds__(256) void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h)
 {
     constexpr int R = 16 / TCH, HALF = R / 2;
     __shared__ float part[TCH][4][kGuRows * 2];  // [tt][wave][gate rows | up rows]
     int e, r_beg, n_e;
-    if (!slot_expert(a, blockIdx.y, e, r_beg, n_e)) return;
+    if (PAIR) {
+        r_beg = blockIdx.y;
+        e = a.topk_idx[r_beg];
+        n_e = 1;
+    } else if (!slot_expert(a, blockIdx.y, e, r_beg, n_e)) {
+        return;
+    }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r0 = blockIdx.x * kGuRows;
     const int d = a.d, nb = d >> 5;
@@ -206,7 +214,7 @@ __global__ __launch_bounds__(256) void gateup_gemv_kernel(FfnArgs a, float* __re
 #pragma unroll
         for (int tt = 0; tt < TCH; ++tt) {
             int m = min(t0 + tt, n_e - 1);
-            int tok = a.perm_pair[r_beg + m] / a.k;
+            int tok = (PAIR ? r_beg : a.perm_pair[r_beg + m]) / a.k;
             float tmp[BPL][32];
             load_act<BPL>(a.x + (size_t)tok * d, tid, 256, nb, tmp);
 #pragma unroll
@@ -354,6 +362,72 @@ __global__ __launch_bounds__(256) void down_gemv_kernel(FfnArgs a, const float* 
 }
 
 // ---------------------------------------------------------------------------
+// Pair-major down with the combine fused, for small batches: block (x, t)
+// owns rows [16x, 16x+16) of y[t]; wave w streams those rows of the experts
+// j = w, w+4, ... of token t (one f-wide row per lane group, BPL blocks per
+// lane), reduces each expert's 16 dot products with one transposed reduction
+// and accumulates w[t,j] * o in j order; the four waves' partial sums are
+// added in wave order.  Deterministic, and no per-pair output is written.
+template <int BPL>
+__global__ __launch_bounds__(256) void down_gather_kernel(FfnArgs a, const float* __restrict__ hbuf,
+                                                          float* __restrict__ y)
+{
+    __shared__ float part[4][16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t = blockIdx.y, c0 = blockIdx.x * 16;
+    const int f = a.f, nb = f >> 5, k = a.k;
+    const size_t crow = (size_t)(f >> 1), srow = (size_t)nb;
+    uint32_t coff[BPL], soffl[BPL];
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+        const int blk = lane + 64 * b;
+        coff[b] = blk < nb ? (uint32_t)blk * 16u : kOff;
+        soffl[b] = blk < nb ? (uint32_t)blk : kOff;
+    }
+    float yacc = 0.f;
+    for (int j = wave; j < k; j += 4) {
+        const int p = t * k + j;
+        const int e = a.topk_idx[p];
+        const float w = a.topk_w[p];
+        const size_t wrow0 = (size_t)e * a.d + c0;
+        const __amdgpu_buffer_rsrc_t rd = weight_rsrc(a.dc + wrow0 * crow);
+        const __amdgpu_buffer_rsrc_t rds = weight_rsrc(a.ds + wrow0 * srow);
+        uint4 q[16][BPL];
+        uint32_t sb[16][BPL];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+#pragma unroll
+            for (int b = 0; b < BPL; ++b) {
+                q[i][b] = ld_codes(rd, coff[b], (uint32_t)i * (uint32_t)crow);
+                sb[i][b] = ld_scale(rds, soffl[b], (uint32_t)i * (uint32_t)srow);
+            }
+        }
+        float hr[BPL][1][32];
+        {
+            float tmp[BPL][32];
+            load_act<BPL>(hbuf + (size_t)p * f, lane, 64, nb, tmp);
+#pragma unroll
+            for (int b = 0; b < BPL; ++b)
+#pragma unroll
+                for (int i = 0; i < 32; ++i) hr[b][0][i] = tmp[b][i];
+        }
+        float acc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float s1[1] = {0.f};
+#pragma unroll
+            for (int b = 0; b < BPL; ++b) dot32_multi<1>(q[i][b], e8m0_f32(sb[i][b]), hr[b], s1);
+            acc[i] = s1[0];
+        }
+        const float v = wave_transpose_sum16(acc);
+        yacc = __builtin_fmaf(w, v, yacc);
+    }
+    if (lane < 16) part[wave][lane] = yacc;
+    __syncthreads();
+    if (tid < 16) y[(size_t)t * a.d + c0 + tid] = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+}
+
+// ---------------------------------------------------------------------------
 // y[t] = sum_j w[t,j] * o[row_of_pair[t*k+j]], j ascending (deterministic).
 __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a, const float* __restrict__ o,
                                                       float* __restrict__ y)
@@ -363,14 +437,28 @@ __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a, const float* __
     const int d4 = a.d >> 2;
     if (c4 >= d4) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < a.k; ++j) {
-        const int p = t * a.k + j;
-        const float w = a.topk_w[p];
-        const float4 v = reinterpret_cast<const float4*>(o + (size_t)a.row_of_pair[p] * a.d)[c4];
-        acc.x = __builtin_fmaf(w, v.x, acc.x);
-        acc.y = __builtin_fmaf(w, v.y, acc.y);
-        acc.z = __builtin_fmaf(w, v.z, acc.z);
-        acc.w = __builtin_fmaf(w, v.w, acc.w);
+    const float4* o4 = reinterpret_cast<const float4*>(o);
+    for (int j0 = 0; j0 < a.k; j0 += 4) {
+        // four pairs at a time, indices clamped so every load is in flight;
+        // the weights of pairs past k are zero and add nothing
+        int row[4];
+        float w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int p = t * a.k + min(j0 + u, a.k - 1);
+            row[u] = a.row_of_pair[p];
+            w[u] = (j0 + u < a.k) ? a.topk_w[p] : 0.0f;
+        }
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = o4[(size_t)row[u] * d4 + c4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            acc.x = __builtin_fmaf(w[u], v[u].x, acc.x);
+            acc.y = __builtin_fmaf(w[u], v[u].y, acc.y);
+            acc.z = __builtin_fmaf(w[u], v[u].z, acc.z);
+            acc.w = __builtin_fmaf(w[u], v[u].w, acc.w);
+        }
     }
     reinterpret_cast<float4*>(y + (size_t)t * a.d)[c4] = acc;
 }
@@ -378,23 +466,39 @@ __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a, const float* __
 // ---------------------------------------------------------------------------
 static int tokens_per_pass(const FfnArgs& a) { return a.T == 1 ? 1 : 2; }
 
-template <int TCH>
+template <int TCH, bool PAIR>
 static void gateup_dispatch(const FfnArgs& a, float* h, hipStream_t s)
 {
     const int nb = a.d / 32;
-    dim3 grid((a.f + kGuRows - 1) / kGuRows, a.nslots);
+    dim3 grid((a.f + kGuRows - 1) / kGuRows, PAIR ? a.P : a.nslots);
     if (nb <= 256)
-        gateup_gemv_kernel<TCH, 1><<<grid, dim3(256), 0, s>>>(a, h);
+        gateup_gemv_kernel<TCH, 1, PAIR><<<grid, dim3(256), 0, s>>>(a, h);
     else
-        gateup_gemv_kernel<TCH, 2><<<grid, dim3(256), 0, s>>>(a, h);  // d <= 16384 (checked)
+        gateup_gemv_kernel<TCH, 2, PAIR><<<grid, dim3(256), 0, s>>>(a, h);  // d <= 16384 (checked)
 }
+
+bool use_pair_path(const FfnArgs& a) { return a.P <= kPairMajorMax && a.f <= 8192; }
 
 void launch_gateup_gemv(const FfnArgs& a, float* h, hipStream_t s)
 {
-    if (tokens_per_pass(a) == 1)
-        gateup_dispatch<1>(a, h, s);
+    if (use_pair_path(a))
+        gateup_dispatch<1, true>(a, h, s);
+    else if (tokens_per_pass(a) == 1)
+        gateup_dispatch<1, false>(a, h, s);
     else
-        gateup_dispatch<2>(a, h, s);
+        gateup_dispatch<2, false>(a, h, s);
+}
+
+void launch_down_gather(const FfnArgs& a, const float* h, float* y, hipStream_t s)
+{
+    const int nb = a.f / 32;
+    dim3 grid(a.d / 16, a.T);
+    if (nb <= 64)
+        down_gather_kernel<1><<<grid, dim3(256), 0, s>>>(a, h, y);
+    else if (nb <= 128)
+        down_gather_kernel<2><<<grid, dim3(256), 0, s>>>(a, h, y);
+    else
+        down_gather_kernel<4><<<grid, dim3(256), 0, s>>>(a, h, y);
 }
 
 template <int TCH, int NK>

@@ -53,7 +53,13 @@ struct FfnArgs {
     const int32_t* active;  // null: slots are sorted rows (segment heads)
     int nslots;
 };
+// Batches with at most kPairMajorMax token-expert pairs (and d_ff <= 8192)
+// take the pair-major path: gate/up per pair, then down with the combine
+// fused (launch_down_gather); larger ones are grouped by expert.
+constexpr int kPairMajorMax = 128;
+bool use_pair_path(const FfnArgs& a);
 void launch_gateup_gemv(const FfnArgs& a, float* h, hipStream_t s);
+void launch_down_gather(const FfnArgs& a, const float* h, float* y, hipStream_t s);
 void launch_down_gemv(const FfnArgs& a, const float* h, float* o, hipStream_t s);
 void launch_combine(const FfnArgs& a, const float* o, float* y, hipStream_t s);
 

@@ -43,26 +43,29 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(
 #pragma unroll
     for (int t = 0; t < kGemvTok; ++t) acc[t] = 0.0;
     for (int base = 0; base < n4; base += 256 * kRouterPerThread) {
+        // branch-free (clamped) loads; lanes past the end multiply by zero
         float4 w[kRouterPerThread];
+        float live[kRouterPerThread];
 #pragma unroll
         for (int j = 0; j < kRouterPerThread; ++j) {
             int i = base + tid + 256 * j;
-            w[j] = (i < n4) ? w4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            w[j] = w4[min(i, n4 - 1)];
+            live[j] = (i < n4) ? 1.0f : 0.0f;
         }
 #pragma unroll
         for (int t = 0; t < kGemvTok; ++t) {
             if (t < T) {
                 const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)t * d);
+                float4 v[kRouterPerThread];
+#pragma unroll
+                for (int j = 0; j < kRouterPerThread; ++j) v[j] = x4[min(base + tid + 256 * j, n4 - 1)];
 #pragma unroll
                 for (int j = 0; j < kRouterPerThread; ++j) {
-                    int i = base + tid + 256 * j;
-                    if (i < n4) {
-                        float4 v = x4[i];
-                        acc[t] = fma((double)w[j].x, (double)v.x, acc[t]);
-                        acc[t] = fma((double)w[j].y, (double)v.y, acc[t]);
-                        acc[t] = fma((double)w[j].z, (double)v.z, acc[t]);
-                        acc[t] = fma((double)w[j].w, (double)v.w, acc[t]);
-                    }
+                    const double m = (double)live[j];
+                    acc[t] = fma((double)w[j].x * m, (double)v[j].x, acc[t]);
+                    acc[t] = fma((double)w[j].y * m, (double)v[j].y, acc[t]);
+                    acc[t] = fma((double)w[j].z * m, (double)v[j].z, acc[t]);
+                    acc[t] = fma((double)w[j].w * m, (double)v[j].w, acc[t]);
                 }
             }
         }
@@ -188,38 +191,54 @@ __device__ int block_exclusive_scan(int v, int* wave_tot, int* total)
 // keys unless the bias steers the selection only).
 constexpr int kMaxPerLane = 16;
 
-template <int M>
-__device__ __forceinline__ int swz_i(int v)
+// (key, expert) of the better candidate: larger key, ties to the lower id;
+// be == INT_MAX marks "no candidate".
+__device__ __forceinline__ bool better(double ok, int oe, double bk, int be)
 {
-    return __builtin_amdgcn_ds_swizzle(v, (M << 10) | 0x1F);
+    return (oe != 0x7fffffff) && (be == 0x7fffffff || ok > bk || (ok == bk && oe < be));
 }
 
-__device__ __forceinline__ int bperm_i(int v, int src_lane)
+// One exchange step of the wave argmax through a DPP lane pattern (VALU
+// latency, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(double& bk, int& be)
 {
-    return __builtin_amdgcn_ds_bpermute(src_lane << 2, v);
-}
-
-template <int M>
-__device__ __forceinline__ void argmax_step(double& bk, int& be)
-{
-    const int lane = threadIdx.x & 63;
     int lo = __double2loint(bk), hi = __double2hiint(bk);
-    int olo, ohi, oe;
-    if (M < 32) {
-        olo = swz_i<M>(lo);
-        ohi = swz_i<M>(hi);
-        oe = swz_i<M>(be);
-    } else {
-        olo = bperm_i(lo, lane ^ 32);
-        ohi = bperm_i(hi, lane ^ 32);
-        oe = bperm_i(be, lane ^ 32);
-    }
+    int olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
+    int ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
+    int oe = __builtin_amdgcn_update_dpp(be, be, CTRL, 0xF, 0xF, false);
     double ok = __hiloint2double(ohi, olo);
-    bool take = (oe != 0x7fffffff) && (be == 0x7fffffff || ok > bk || (ok == bk && oe < be));
-    if (take) {
+    if (better(ok, oe, bk, be)) {
         bk = ok;
         be = oe;
     }
+}
+
+// Wave-wide argmax: within each row of 16 lanes by DPP (quad swaps, then
+// rotations by 4 and 8), then the four row winners compared as uniform values.
+__device__ __forceinline__ void wave_argmax(double& bk, int& be)
+{
+    argmax_dpp<0xB1>(bk, be);   // quad_perm [1,0,3,2]
+    argmax_dpp<0x4E>(bk, be);   // quad_perm [2,3,0,1]
+    argmax_dpp<0x124>(bk, be);  // row_ror:4
+    argmax_dpp<0x128>(bk, be);  // row_ror:8
+    int lo = __double2loint(bk), hi = __double2hiint(bk);
+    double rk = bk;
+    int re = be;
+    rk = __hiloint2double(__builtin_amdgcn_readlane(hi, 0), __builtin_amdgcn_readlane(lo, 0));
+    re = __builtin_amdgcn_readlane(be, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+        double ok = __hiloint2double(__builtin_amdgcn_readlane(hi, 16 * r),
+                                     __builtin_amdgcn_readlane(lo, 16 * r));
+        int oe = __builtin_amdgcn_readlane(be, 16 * r);
+        if (better(ok, oe, rk, re)) {
+            rk = ok;
+            re = oe;
+        }
+    }
+    bk = rk;
+    be = re;
 }
 
 __device__ void wave_topk(int E, int k, const double* __restrict__ lrow,
@@ -227,18 +246,21 @@ __device__ void wave_topk(int E, int k, const double* __restrict__ lrow,
                           int* sel_e_out, int32_t* idx_out, float* w_out)
 {
     const int lane = threadIdx.x & 63;
+    // branch-free loads (clamped index) so all of them are in flight at once
     double key[kMaxPerLane];
     uint32_t taken = 0;
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
-        int e = lane + 64 * i;
-        if (e < E) {
-            double l = lrow[e];
-            key[i] = bias_select_only ? l + (double)bias[e] : l;
-        } else {
-            key[i] = 0.0;
-            taken |= 1u << i;
-        }
+        const int e = lane + 64 * i;
+        key[i] = lrow[min(e, E - 1)];
+        if (e >= E) taken |= 1u << i;
+    }
+    if (bias_select_only) {
+        float b[kMaxPerLane];
+#pragma unroll
+        for (int i = 0; i < kMaxPerLane; ++i) b[i] = bias[min(lane + 64 * i, E - 1)];
+#pragma unroll
+        for (int i = 0; i < kMaxPerLane; ++i) key[i] += (double)b[i];
     }
     int my_e = 0;
     for (int j = 0; j < k; ++j) {
@@ -252,12 +274,7 @@ __device__ void wave_topk(int E, int k, const double* __restrict__ lrow,
                 be = lane + 64 * i;
             }
         }
-        argmax_step<1>(bk, be);
-        argmax_step<2>(bk, be);
-        argmax_step<4>(bk, be);
-        argmax_step<8>(bk, be);
-        argmax_step<16>(bk, be);
-        argmax_step<32>(bk, be);
+        wave_argmax(bk, be);
         if ((be & 63) == lane) taken |= 1u << (be >> 6);
         if (lane == j) my_e = be;
     }

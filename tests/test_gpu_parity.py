@@ -196,6 +196,16 @@ def test_k3_decode_t1(k3layer):
         assert np.array_equal(y, y2), "decode output is not bitwise deterministic"
 
 
+def test_k3_small_batch_t8(k3layer):
+    """Pair-major path (gate/up per pair, down with the fused gather combine)."""
+    sh = k3layer["shape"]
+    x = synthdata.tokens(sh, 8, first=20000)
+    y, route = _run(x, k3layer["wr_dev"], k3layer["dev"], sh.k)
+    ref = oracle.route(x, k3layer["wr"], sh.k)
+    assert_route_equal(route, ref)
+    assert_y_close(y, oracle_y(x, ref, range(8), k3layer["get"]))
+
+
 def test_k3_batch_t64(k3layer):
     sh = k3layer["shape"]
     x = synthdata.tokens(sh, 64)
