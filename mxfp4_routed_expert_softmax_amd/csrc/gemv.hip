@@ -363,18 +363,22 @@ __global__ __launch_bounds__(256) void down_gemv_kernel(FfnArgs a, const float* 
 
 // ---------------------------------------------------------------------------
 // Pair-major down with the combine fused, for small batches: block (x, t)
-// owns rows [16x, 16x+16) of y[t]; wave w streams those rows of the experts
-// j = w, w+4, ... of token t (one f-wide row per lane group, BPL blocks per
-// lane), reduces each expert's 16 dot products with one transposed reduction
-// and accumulates w[t,j] * o in j order; the four waves' partial sums are
+// owns RW rows [RW*x, RW*x+RW) of y[t] (RW = d/256 when that divides, so
+// every CU gets the same share); wave w streams those rows of the experts
+// j = w, w+8, ... of token t (one f-wide row per lane, BPL blocks per lane)
+// in batches of 16 rows, reduces each batch with one transposed reduction
+// and accumulates w[t,j] * o in j order; the eight waves' partial sums are
 // added in wave order.  Deterministic, and no per-pair output is written.
-template <int BPL>
-__global__ __launch_bounds__(256) void down_gather_kernel(FfnArgs a, const float* __restrict__ hbuf,
-                                                          float* __restrict__ y)
+constexpr int kGatherWaves = 8;
+
+template <int RW, int BPL>
+__global__ __launch_bounds__(64 * kGatherWaves) void down_gather_kernel(FfnArgs a, const float* __restrict__ hbuf,
+                                                                        float* __restrict__ y)
 {
-    __shared__ float part[4][16];
+    constexpr int NBT = (RW + 15) / 16;
+    __shared__ float part[kGatherWaves][RW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int t = blockIdx.y, c0 = blockIdx.x * 16;
+    const int t = blockIdx.y, c0 = blockIdx.x * RW;
     const int f = a.f, nb = f >> 5, k = a.k;
     const size_t crow = (size_t)(f >> 1), srow = (size_t)nb;
     uint32_t coff[BPL], soffl[BPL];
@@ -384,24 +388,16 @@ __global__ __launch_bounds__(256) void down_gather_kernel(FfnArgs a, const float
         coff[b] = blk < nb ? (uint32_t)blk * 16u : kOff;
         soffl[b] = blk < nb ? (uint32_t)blk : kOff;
     }
-    float yacc = 0.f;
-    for (int j = wave; j < k; j += 4) {
+    float yacc[NBT];
+#pragma unroll
+    for (int bt = 0; bt < NBT; ++bt) yacc[bt] = 0.f;
+    for (int j = wave; j < k; j += kGatherWaves) {
         const int p = t * k + j;
         const int e = a.topk_idx[p];
         const float w = a.topk_w[p];
         const size_t wrow0 = (size_t)e * a.d + c0;
         const __amdgpu_buffer_rsrc_t rd = weight_rsrc(a.dc + wrow0 * crow);
         const __amdgpu_buffer_rsrc_t rds = weight_rsrc(a.ds + wrow0 * srow);
-        uint4 q[16][BPL];
-        uint32_t sb[16][BPL];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-#pragma unroll
-            for (int b = 0; b < BPL; ++b) {
-                q[i][b] = ld_codes(rd, coff[b], (uint32_t)i * (uint32_t)crow);
-                sb[i][b] = ld_scale(rds, soffl[b], (uint32_t)i * (uint32_t)srow);
-            }
-        }
         float hr[BPL][1][32];
         {
             float tmp[BPL][32];
@@ -411,20 +407,46 @@ __global__ __launch_bounds__(256) void down_gather_kernel(FfnArgs a, const float
 #pragma unroll
                 for (int i = 0; i < 32; ++i) hr[b][0][i] = tmp[b][i];
         }
-        float acc[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float s1[1] = {0.f};
+        for (int bt = 0; bt < NBT; ++bt) {
+            uint4 q[16][BPL];
+            uint32_t sb[16][BPL];
 #pragma unroll
-            for (int b = 0; b < BPL; ++b) dot32_multi<1>(q[i][b], e8m0_f32(sb[i][b]), hr[b], s1);
-            acc[i] = s1[0];
+            for (int i = 0; i < 16; ++i) {
+                const int row = 16 * bt + i;
+#pragma unroll
+                for (int b = 0; b < BPL; ++b) {
+                    if (row < RW) {
+                        q[i][b] = ld_codes(rd, coff[b], (uint32_t)row * (uint32_t)crow);
+                        sb[i][b] = ld_scale(rds, soffl[b], (uint32_t)row * (uint32_t)srow);
+                    } else {
+                        q[i][b] = make_uint4(0u, 0u, 0u, 0u);
+                        sb[i][b] = 127u;
+                    }
+                }
+            }
+            float acc[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float s1[1] = {0.f};
+#pragma unroll
+                for (int b = 0; b < BPL; ++b) dot32_multi<1>(q[i][b], e8m0_f32(sb[i][b]), hr[b], s1);
+                acc[i] = s1[0];
+            }
+            const float v = wave_transpose_sum16(acc);
+            yacc[bt] = __builtin_fmaf(w, v, yacc[bt]);
         }
-        const float v = wave_transpose_sum16(acc);
-        yacc = __builtin_fmaf(w, v, yacc);
     }
-    if (lane < 16) part[wave][lane] = yacc;
+#pragma unroll
+    for (int bt = 0; bt < NBT; ++bt)
+        if (lane < 16 && 16 * bt + lane < RW) part[wave][16 * bt + lane] = yacc[bt];
     __syncthreads();
-    if (tid < 16) y[(size_t)t * a.d + c0 + tid] = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+    if (tid < RW) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kGatherWaves; ++w) sum += part[w][tid];
+        y[(size_t)t * a.d + c0 + tid] = sum;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -489,16 +511,26 @@ void launch_gateup_gemv(const FfnArgs& a, float* h, hipStream_t s)
         gateup_dispatch<2, false>(a, h, s);
 }
 
-void launch_down_gather(const FfnArgs& a, const float* h, float* y, hipStream_t s)
+template <int RW>
+static void down_gather_dispatch(const FfnArgs& a, const float* h, float* y, hipStream_t s)
 {
     const int nb = a.f / 32;
-    dim3 grid(a.d / 16, a.T);
+    dim3 grid(a.d / RW, a.T);
     if (nb <= 64)
-        down_gather_kernel<1><<<grid, dim3(256), 0, s>>>(a, h, y);
+        down_gather_kernel<RW, 1><<<grid, dim3(64 * kGatherWaves), 0, s>>>(a, h, y);
     else if (nb <= 128)
-        down_gather_kernel<2><<<grid, dim3(256), 0, s>>>(a, h, y);
+        down_gather_kernel<RW, 2><<<grid, dim3(64 * kGatherWaves), 0, s>>>(a, h, y);
     else
-        down_gather_kernel<4><<<grid, dim3(256), 0, s>>>(a, h, y);
+        down_gather_kernel<RW, 4><<<grid, dim3(64 * kGatherWaves), 0, s>>>(a, h, y);
+}
+
+void launch_down_gather(const FfnArgs& a, const float* h, float* y, hipStream_t s)
+{
+    // 28 rows per block gives exactly one block per CU at d_model 7168
+    if (a.d % 28 == 0 && a.d / 28 >= 256)
+        down_gather_dispatch<28>(a, h, y, s);
+    else
+        down_gather_dispatch<16>(a, h, y, s);
 }
 
 template <int TCH, int NK>
