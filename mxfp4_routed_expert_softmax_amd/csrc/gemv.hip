@@ -178,8 +178,10 @@ constexpr int kGuRows = 32;  // row pairs per block
 
 // PAIR: the pair-major variant for small batches -- block y serves pair
 // p = t*k + j alone (expert topk_idx[p], token t, h row p), no grouping.
+// 4 waves per SIMD: all four blocks a CU receives at d_model 7168 are resident at once
 template <int TCH, int BPL, bool PAIR>
-__global__ __launch_bounds__(256) void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BPL == 1 && TCH == 1 ? 4 : 1, 8)))
+void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h)
 {
     constexpr int R = 16 / TCH, HALF = R / 2;
     __shared__ float part[TCH][4][kGuRows * 2];  // [tt][wave][gate rows | up rows]
