@@ -22,6 +22,11 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# the kernel sources whose counters profiles/traffic.json records
+TRAFFIC_SOURCES = ["mxfp4_routed_expert_softmax_amd/csrc/" + f for f in
+                   ("gemv.hip", "mx.hip", "route.hip", "api.hip", "device_common.h", "kernels.h")]
+FFN_KERNELS = ("gateup_", "down_", "combine_", "quantize_rows", "zero_kernel", "active_list")
 MXFP4_PEAK_TFLOPS = 10100.0  # dense MXFP4 matrix peak
 
 
@@ -39,6 +44,9 @@ def parse():
                     help="budget of host time for the oracle baseline (0 disables it)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step from a captured HIP graph instead of eager launches")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB three times "
+                         "(reference kernel for hardware byte counters; not part of the step)")
     return ap.parse_args()
 
 
@@ -128,12 +136,22 @@ def main():
         ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
         achieved = (expert_bytes + act_bytes) / (ffn_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": "expert FFN stage (k3moe_ffn: gate/up GEMV + down GEMV + combine)",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
+                    "kernel": "expert FFN stage (every kernel k3moe_ffn launches; decode: gate/up GEMV "
+                              "with SwiGLU + down GEMV with the fused combine)",
                     "bytes_per_launch": expert_bytes + act_bytes, "avg_ms": round(ffn_ms, 5)}
     if wl.act_mode == "mxfp4" and roofline is not None:
         flops = 2.0 * 3 * sh.d * sh.f * T * sh.k
         roofline["mfma_frac"] = round(flops / (roofline["avg_ms"] * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS, 4)
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -161,6 +179,28 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic(workload):
+    """HBM bytes per expert-FFN launch from the committed counter profile
+    (FETCH_SIZE / WRITE_SIZE scaled by a plain-copy calibration), or None
+    when the kernel sources changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest()[:16] != rec.get("source_sha") or workload not in rec.get("workloads", {}):
+        return None
+    w = rec["workloads"][workload]
+    total = 0.0
+    for name, v in w["kernels"].items():
+        if any(key in name for key in FFN_KERNELS):
+            total += (v["fetch_kib"] * w["fetch_scale"] + v["write_kib"] * w["write_scale"]) * 1024
+    return round(total)
 
 
 def cpu_baseline(sh, wl, budget_s):
