@@ -136,8 +136,8 @@ int k3moe_route(const k3moe_dims *dims, const float *x, const float *w_router,
 /* Expert FFN and combine, from the outputs of k3moe_route (device pointers).
  *   y  fp32 [T][d_model], fully overwritten.
  *   dbg optional (NULL or a host struct of device pointers), MXFP4 mode only.
- * In K3MOE_ACT_FP32 mode y is bit-deterministic; in K3MOE_ACT_MXFP4 mode the
- * combine is a scatter-add whose fp32 summation order may vary run to run. */
+ * y is bit-deterministic in both modes: the combine adds the k expert
+ * outputs of a token in a fixed order (no atomics). */
 int k3moe_ffn(const k3moe_dims *dims, const float *x, const k3moe_experts *experts,
               const int32_t *topk_idx, const float *topk_w, const int32_t *counts,
               const int32_t *offsets, const int32_t *perm_pair,

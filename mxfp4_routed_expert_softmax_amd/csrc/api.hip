@@ -34,6 +34,7 @@ WsLayout ws_layout(int T, int E, int k, int d, int f, int act_mode)
         L.xq_scales = take((size_t)T * d / 32);
         L.hq_codes = take(P * f / 2);
         L.hq_scales = take(P * f / 32);
+        L.o = take(P * d * sizeof(float));
     }
     L.total = off;
     return L;
@@ -241,8 +242,9 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
         }
         launch_gateup_mfma(a, xqc, xqs, hqc, hqs, dbg ? dbg->h : nullptr,
                            dbg ? dbg->h_codes : nullptr, dbg ? dbg->h_scales : nullptr, s);
-        launch_zero(y, (size_t)a.T * a.d, s);
-        launch_down_mfma(a, hqc, hqs, y, s);
+        float* o = reinterpret_cast<float*>(ws + L.o);
+        launch_down_mfma(a, hqc, hqs, y, o, s);
+        launch_combine(a, o, y, s);
     }
     return K3MOE_OK;
 }

@@ -157,14 +157,162 @@ __device__ __forceinline__ void load_frag128(const uint8_t* crow, const uint8_t*
 }
 
 // ---------------------------------------------------------------------------
-// gate/up GEMM: block = 4 waves, wave w owns f rows [n0 + 32w, +32) as two
-// 16-row subtiles of both gate and up; M = the expert's tokens in tiles of
-// 16, MT tiles per pass.  Epilogue: h = silu(g) * u in fp32, then the MX
-// quantiser over each token's 32 consecutive f values (exactly the wave's
-// two subtiles), written to h_q rows in grouped order.
-constexpr int kMT = 8;
+// Tile order: the hardware deals consecutive workgroups round-robin to the 8
+// XCDs, each with its own L2.  Experts go round-robin to XCDs (slot s -> XCD
+// s % 8) and each XCD receives the n-tiles of one expert back to back, so an
+// expert's activation rows are read from HBM once and from that XCD's L2 by
+// its other tiles; busy and idle experts spread evenly over the XCDs.
+constexpr int kXcds = 8;
 
-__global__ __launch_bounds__(256) void gateup_mfma_kernel(FfnArgs a, const uint8_t* __restrict__ xqc,
+__device__ __forceinline__ bool xcd_tile(int bid, int nslots, int ntiles, int& slot, int& tile)
+{
+    const int x = bid % kXcds, pos = bid / kXcds;
+    slot = x + kXcds * (pos / ntiles);
+    tile = pos % ntiles;
+    return slot < nslots;
+}
+
+static int xcd_grid(int nslots, int ntiles)
+{
+    return kXcds * ((nslots + kXcds - 1) / kXcds) * ntiles;
+}
+
+// ---------------------------------------------------------------------------
+// Grouped scaled-MFMA GEMM building blocks.  A = activation rows of one
+// expert (x_q rows of its tokens, or its h_q rows), staged per 512-wide K
+// chunk in LDS: row m holds 256 code bytes then the chunk's 16 scale bytes
+// (272-byte stride, which also spreads rows over the LDS banks); two buffers,
+// the next chunk is fetched into registers while the current one is used.
+// B = weight rows, loaded straight into registers (each weight byte is used
+// by exactly one wave), also one chunk ahead.
+constexpr int kMT = 8;             // 16-token tiles per pass (M <= 128)
+constexpr int kARow = 272;         // LDS bytes per staged activation row
+constexpr int kAStage = 16 * kMT * kARow;
+
+// Stage the A chunk kc into an LDS buffer with the gfx950 direct
+// global->LDS load (lane l of a wave instruction lands at M0 + 16*l): item
+// it = 17*r + c (16 code pieces then the scale piece of row r) goes to LDS
+// byte 16*it, i.e. row r at r*kARow.  Rows past the expert's tokens repeat its
+// last row; their outputs are discarded.
+__device__ __forceinline__ void a_issue(const uint8_t* const* rows_c, const uint8_t* const* rows_s, int nrows,
+                                        int mt_n, int kc, uint8_t* dst)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n_items = 16 * mt_n * 17;  // a multiple of 64 when mt_n is even; else the tail is masked
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+        const int base = 256 * i + 64 * wave;
+        if (base >= n_items) break;
+        const int it = base + lane;
+        if (it < n_items) {
+            const int r = min(it / 17, nrows - 1), c = it - (it / 17) * 17;
+            const uint8_t* src = c < 16 ? rows_c[r] + (kc >> 1) + 16 * c : rows_s[r] + (kc >> 5);
+            __builtin_amdgcn_global_load_lds(src, dst + 16 * base, 16, 0, 0);
+        }
+    }
+}
+
+// A fragment of M-tile mt for this lane (row 16*mt + li, quarter g)
+__device__ __forceinline__ void a_frag(const uint8_t* lds, int mt, int li, int g, Frag512& f)
+{
+    const uint8_t* row = lds + (16 * mt + li) * kARow;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.q[i] = *reinterpret_cast<const uint4*>(row + 64 * g + 16 * i);
+    f.s = *reinterpret_cast<const uint32_t*>(row + 256 + 4 * g);
+}
+
+template <int NB>
+__device__ __forceinline__ void b_fetch(Frag512 (&F)[NB], const uint8_t* const (&bc)[NB],
+                                        const uint8_t* const (&bs)[NB], int kc, int g)
+{
+#pragma unroll
+    for (int s = 0; s < NB; ++s) load_frag512(bc[s], bs[s], kc, g, F[s]);
+}
+
+// M-tiles one at a time, the next tile's A fragment read from LDS while the
+// current one is on the matrix cores (keeps at most two fragments live)
+template <int NB>
+__device__ __forceinline__ void mma_chunk(const Frag512 (&F)[NB], const uint8_t* lds, int mt_n, int li, int g,
+                                          f32x4 (&c)[kMT][NB])
+{
+    Frag512 fa, fn;
+    a_frag(lds, 0, li, g, fa);
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+        if (mt < mt_n) {
+            if (mt + 1 < mt_n) a_frag(lds, mt + 1, li, g, fn);
+#pragma unroll
+            for (int s = 0; s < NB; ++s) {
+                c[mt][s] = mfma_fp4<0>(fa.q[0], F[s].q[0], fa.s, F[s].s, c[mt][s]);
+                c[mt][s] = mfma_fp4<1>(fa.q[1], F[s].q[1], fa.s, F[s].s, c[mt][s]);
+                c[mt][s] = mfma_fp4<2>(fa.q[2], F[s].q[2], fa.s, F[s].s, c[mt][s]);
+                c[mt][s] = mfma_fp4<3>(fa.q[3], F[s].q[3], fa.s, F[s].s, c[mt][s]);
+            }
+            fa = fn;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// The K loop of one M pass (K % 512 == 0): LDS double buffer for A filled by
+// DMA one chunk ahead; the B fragments of a chunk are loaded at its start
+// (their latency overlaps the other resident waves' matrix work).
+template <int NB>
+__device__ __forceinline__ void gemm_pass512(const uint8_t* const* rows_c, const uint8_t* const* rows_s, int nrows,
+                                             const uint8_t* const (&bc)[NB], const uint8_t* const (&bs)[NB],
+                                             int K, int mt_n, int li, int g, uint8_t* lds, f32x4 (&c)[kMT][NB])
+{
+    Frag512 F[NB];
+    a_issue(rows_c, rows_s, nrows, mt_n, 0, lds);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int buf = 0;
+    for (int kc = 0; kc < K; kc += 512) {
+        b_fetch<NB>(F, bc, bs, kc, g);
+        const bool more = kc + 512 < K;
+        if (more) a_issue(rows_c, rows_s, nrows, mt_n, kc + 512, lds + (buf ^ 1) * kAStage);
+        mma_chunk<NB>(F, lds + buf * kAStage, mt_n, li, g, c);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // next buffer landed; every wave is done with this one
+        buf ^= 1;
+    }
+}
+
+// 128-wide K steps for reduction axes that are not a multiple of 512 (small
+// layers); A straight from global memory.
+template <int NB>
+__device__ __forceinline__ void gemm_pass128(const uint8_t* const* rows_c, const uint8_t* const* rows_s, int nrows,
+                                             const uint8_t* const (&bc)[NB], const uint8_t* const (&bs)[NB],
+                                             int K, int mt_n, int li, int g, f32x4 (&c)[kMT][NB])
+{
+    for (int kc = 0; kc < K; kc += 128) {
+        uint4 qb[NB];
+        uint32_t sb[NB];
+#pragma unroll
+        for (int s = 0; s < NB; ++s) load_frag128(bc[s], bs[s], kc, g, K, qb[s], sb[s]);
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+            if (mt < mt_n) {
+                const int r = min(16 * mt + li, nrows - 1);
+                uint4 qa;
+                uint32_t sa;
+                load_frag128(rows_c[r], rows_s[r], kc, g, K, qa, sa);
+#pragma unroll
+                for (int s = 0; s < NB; ++s) c[mt][s] = mfma_fp4<0>(qa, qb[s], sa, sb[s], c[mt][s]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gate/up GEMM: block = 4 waves, n-tile = 64 f rows; wave w owns gate rows
+// and up rows [n0 + 16w, +16).  M = the expert's tokens, up to 128 per pass.
+// Epilogue: h = silu(g) * u in fp32; the MX quantiser runs over each token's
+// 32 consecutive f values, held by two neighbouring waves' subtiles, so the
+// block exchanges h through LDS once per pass.
+constexpr int kGuTile = 64;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_mfma_kernel(FfnArgs a, const uint8_t* __restrict__ xqc,
                                                           const uint8_t* __restrict__ xqs,
                                                           uint8_t* __restrict__ hqc,
                                                           uint8_t* __restrict__ hqs,
@@ -172,140 +320,98 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(FfnArgs a, const uint8
                                                           uint8_t* __restrict__ dbg_hc,
                                                           uint8_t* __restrict__ dbg_hs)
 {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kAStage];
+    __shared__ const uint8_t* rows_c[16 * kMT];
+    __shared__ const uint8_t* rows_s[16 * kMT];
+    const int ntiles = (a.f + kGuTile - 1) / kGuTile;
+    int slot, ftile;
+    if (!xcd_tile(blockIdx.x, a.nslots, ntiles, slot, ftile)) return;
     int e, r_beg, n_e;
-    if (!mx_slot_expert(a, blockIdx.y, e, r_beg, n_e)) return;
+    if (!mx_slot_expert(a, slot, e, r_beg, n_e)) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;
-    const int nw = blockIdx.x * 128 + wave * 32;
-    if (nw >= a.f) return;
+    const int n0 = ftile * kGuTile;
+    const int nrow_w = min(n0 + 16 * wave, a.f - 16);  // f % 32 == 0: a partial tile repeats rows, masked below
     const int K = a.d;
     const size_t crow = (size_t)(K >> 1), srow = (size_t)(K >> 5);
-    const bool ch512 = (K % 512) == 0;
-    // B rows this lane feeds: gate/up rows nw + 16*s + li
-    const uint8_t *bgc[2], *bgs[2], *buc[2], *bus[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        size_t wr = (size_t)e * a.f + nw + 16 * s + li;
-        bgc[s] = a.gc + wr * crow;
-        bgs[s] = a.gs + wr * srow;
-        buc[s] = a.uc + wr * crow;
-        bus[s] = a.us + wr * srow;
+    const uint8_t* bc[2];
+    const uint8_t* bs[2];
+    {
+        const size_t wr = (size_t)e * a.f + nrow_w + li;
+        bc[0] = a.gc + wr * crow;
+        bs[0] = a.gs + wr * srow;
+        bc[1] = a.uc + wr * crow;
+        bs[1] = a.us + wr * srow;
     }
+    float* hx = reinterpret_cast<float*>(lds);  // h exchange after the K loop: [128][64] fp32 = 32 KB
     for (int m0 = 0; m0 < n_e; m0 += 16 * kMT) {
-        const int mt_n = min(kMT, (n_e - m0 + 15) >> 4);
-        // A rows this lane feeds: token of grouped row r_beg + m0 + 16*mt + li (clamped)
-        const uint8_t *axc[kMT], *axs[kMT];
+        const int nrows = min(16 * kMT, n_e - m0);
+        const int mt_n = (nrows + 15) >> 4;
+        if (threadIdx.x < 16 * kMT) {
+            const int m = min(m0 + (int)threadIdx.x, n_e - 1);
+            const int tok = a.perm_pair[r_beg + m] / a.k;
+            rows_c[threadIdx.x] = xqc + (size_t)tok * crow;
+            rows_s[threadIdx.x] = xqs + (size_t)tok * srow;
+        }
+        __syncthreads();
+        f32x4 c[kMT][2];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
-            int m = min(m0 + 16 * mt + li, n_e - 1);
-            int tok = a.perm_pair[r_beg + m] / a.k;
-            axc[mt] = xqc + (size_t)tok * crow;
-            axs[mt] = xqs + (size_t)tok * srow;
+            c[mt][0] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            c[mt][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
-        f32x4 cg[kMT][2], cu[kMT][2];
+        if ((K % 512) == 0)
+            gemm_pass512<2>(rows_c, rows_s, nrows, bc, bs, K, mt_n, li, g, lds, c);
+        else
+            gemm_pass128<2>(rows_c, rows_s, nrows, bc, bs, K, mt_n, li, g, c);
+        // h of this wave's 16 columns -> LDS [m][16*wave + col]
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt)
+        for (int mt = 0; mt < kMT; ++mt) {
+            if (mt < mt_n) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                cg[mt][s] = (f32x4){0.f, 0.f, 0.f, 0.f};
-                cu[mt][s] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            }
-        int kc = 0;
-        if (ch512) {
-            for (; kc < K; kc += 512) {
-                Frag512 fg[2], fu[2];
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    load_frag512(bgc[s], bgs[s], kc, g, fg[s]);
-                    load_frag512(buc[s], bus[s], kc, g, fu[s]);
-                }
-#pragma unroll
-                for (int mt = 0; mt < kMT; ++mt) {
-                    if (mt < mt_n) {
-                        Frag512 fa;
-                        load_frag512(axc[mt], axs[mt], kc, g, fa);
-#pragma unroll
-                        for (int s = 0; s < 2; ++s) {
-                            cg[mt][s] = mfma_fp4<0>(fa.q[0], fg[s].q[0], fa.s, fg[s].s, cg[mt][s]);
-                            cu[mt][s] = mfma_fp4<0>(fa.q[0], fu[s].q[0], fa.s, fu[s].s, cu[mt][s]);
-                            cg[mt][s] = mfma_fp4<1>(fa.q[1], fg[s].q[1], fa.s, fg[s].s, cg[mt][s]);
-                            cu[mt][s] = mfma_fp4<1>(fa.q[1], fu[s].q[1], fa.s, fu[s].s, cu[mt][s]);
-                            cg[mt][s] = mfma_fp4<2>(fa.q[2], fg[s].q[2], fa.s, fg[s].s, cg[mt][s]);
-                            cu[mt][s] = mfma_fp4<2>(fa.q[2], fu[s].q[2], fa.s, fu[s].s, cu[mt][s]);
-                            cg[mt][s] = mfma_fp4<3>(fa.q[3], fg[s].q[3], fa.s, fg[s].s, cg[mt][s]);
-                            cu[mt][s] = mfma_fp4<3>(fa.q[3], fu[s].q[3], fa.s, fu[s].s, cu[mt][s]);
-                        }
-                    }
-                }
-            }
-        } else {
-            for (; kc < K; kc += 128) {
-                uint4 qg[2], qu[2];
-                uint32_t sg[2], su[2];
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    load_frag128(bgc[s], bgs[s], kc, g, K, qg[s], sg[s]);
-                    load_frag128(buc[s], bus[s], kc, g, K, qu[s], su[s]);
-                }
-#pragma unroll
-                for (int mt = 0; mt < kMT; ++mt) {
-                    if (mt < mt_n) {
-                        uint4 qa;
-                        uint32_t sa;
-                        load_frag128(axc[mt], axs[mt], kc, g, K, qa, sa);
-#pragma unroll
-                        for (int s = 0; s < 2; ++s) {
-                            cg[mt][s] = mfma_fp4<0>(qa, qg[s], sa, sg[s], cg[mt][s]);
-                            cu[mt][s] = mfma_fp4<0>(qa, qu[s], sa, su[s], cu[mt][s]);
-                        }
-                    }
+                for (int v = 0; v < 4; ++v) {
+                    const int m = 16 * mt + 4 * g + v;
+                    hx[m * kGuTile + 16 * wave + li] = silu_f32(c[mt][0][v]) * c[mt][1][v];
                 }
             }
         }
-        // epilogue: lane (li, g) holds rows m = 4g + v, column li of each subtile
+        __syncthreads();
+        // quantise: one thread per (token row, 32-column block): 128 x 2 items
+        for (int it = threadIdx.x; it < nrows * (kGuTile / 32); it += 256) {
+            const int m = it >> 1, hb = it & 1;
+            const int col0 = n0 + 32 * hb;
+            if (col0 < a.f) {
+                const float* hv = hx + m * kGuTile + 32 * hb;
+                float amax = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-            if (mt >= mt_n) break;
+                for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(hv[i]));
+                const uint32_t byte = mx_scale_byte(amax);
+                const float inv = mx_inv_scale(byte);
+                uint32_t w4[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int m = m0 + 16 * mt + 4 * g + v;
-                float h0 = silu_f32(cg[mt][0][v]) * cu[mt][0][v];
-                float h1 = silu_f32(cg[mt][1][v]) * cu[mt][1][v];
-                float amax = fmaxf(fabsf(h0), fabsf(h1));
-                amax = fmaxf(amax, __shfl_xor(amax, 8, 16));
-                amax = fmaxf(amax, __shfl_xor(amax, 4, 16));
-                amax = fmaxf(amax, __shfl_xor(amax, 2, 16));
-                amax = fmaxf(amax, __shfl_xor(amax, 1, 16));
-                uint32_t byte = mx_scale_byte(amax);
-                float inv = mx_inv_scale(byte);
-                uint32_t q0 = e2m1_encode(h0, inv), q1 = e2m1_encode(h1, inv);
-                uint32_t p0 = __shfl_xor(q0, 1, 16), p1 = __shfl_xor(q1, 1, 16);
-                if (m < n_e) {
-                    const size_t r = (size_t)(r_beg + m);
-                    const int blk = nw >> 5;
-                    const size_t fcb = (size_t)(a.f >> 1), fsb = (size_t)(a.f >> 5);
-                    int pair = -1;
-                    if (dbg_h || dbg_hc || dbg_hs) pair = a.perm_pair[r];
-                    if ((li & 1) == 0) {
-                        uint8_t b0 = (uint8_t)(q0 | (p0 << 4)), b1 = (uint8_t)(q1 | (p1 << 4));
-                        hqc[r * fcb + 16 * blk + (li >> 1)] = b0;
-                        hqc[r * fcb + 16 * blk + 8 + (li >> 1)] = b1;
-                        if (dbg_hc) {
-                            dbg_hc[(size_t)pair * fcb + 16 * blk + (li >> 1)] = b0;
-                            dbg_hc[(size_t)pair * fcb + 16 * blk + 8 + (li >> 1)] = b1;
-                        }
-                    }
-                    if (li == 0) {
-                        hqs[r * fsb + blk] = (uint8_t)byte;
-                        if (dbg_hs) dbg_hs[(size_t)pair * fsb + blk] = (uint8_t)byte;
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t wv = 0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) wv |= e2m1_encode(hv[8 * q + i], inv) << (4 * i);
+                    w4[q] = wv;
+                }
+                const size_t r = (size_t)(r_beg + m0 + m);
+                const size_t fcb = (size_t)(a.f >> 1), fsb = (size_t)(a.f >> 5);
+                const int blk = col0 >> 5;
+                *reinterpret_cast<uint4*>(hqc + r * fcb + 16 * blk) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+                hqs[r * fsb + blk] = (uint8_t)byte;
+                if (dbg_h || dbg_hc || dbg_hs) {
+                    const int pair = a.perm_pair[r];
+                    if (dbg_hc) *reinterpret_cast<uint4*>(dbg_hc + (size_t)pair * fcb + 16 * blk) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+                    if (dbg_hs) dbg_hs[(size_t)pair * fsb + blk] = (uint8_t)byte;
                     if (dbg_h) {
-                        dbg_h[(size_t)pair * a.f + nw + li] = h0;
-                        dbg_h[(size_t)pair * a.f + nw + 16 + li] = h1;
+#pragma unroll
+                        for (int i = 0; i < 32; ++i) dbg_h[(size_t)pair * a.f + col0 + i] = hv[i];
                     }
                 }
             }
         }
+        __syncthreads();
     }
 }
 
@@ -313,90 +419,64 @@ void launch_gateup_mfma(const FfnArgs& a, const uint8_t* xq_codes, const uint8_t
                         uint8_t* hq_codes, uint8_t* hq_scales, float* dbg_h, uint8_t* dbg_hc,
                         uint8_t* dbg_hs, hipStream_t s)
 {
-    dim3 grid((a.f + 127) / 128, a.nslots);
-    gateup_mfma_kernel<<<grid, dim3(256), 0, s>>>(a, xq_codes, xq_scales, hq_codes, hq_scales, dbg_h,
-                                                  dbg_hc, dbg_hs);
+    const int grid = xcd_grid(a.nslots, (a.f + kGuTile - 1) / kGuTile);
+    gateup_mfma_kernel<<<dim3(grid), dim3(256), 0, s>>>(a, xq_codes, xq_scales, hq_codes, hq_scales, dbg_h,
+                                                        dbg_hc, dbg_hs);
 }
 
 // ---------------------------------------------------------------------------
-// down GEMM: block = 4 waves, wave w owns d rows [n0 + 64w, +64) as four
-// 16-row subtiles; A = the expert's h_q rows (contiguous in grouped order).
-// Epilogue: y[t][c] += w[t,j] * o[c], fp32 atomic add (the combine).
-__global__ __launch_bounds__(256) void down_mfma_kernel(FfnArgs a, const uint8_t* __restrict__ hqc,
+// down GEMM: block = 4 waves, n-tile = 128 d rows; wave w owns rows
+// [n0 + 32w, +32) as two 16-row subtiles; A = the expert's h_q rows
+// (contiguous in grouped order).  Epilogue: y[t][c] += w[t,j] * o[c], fp32
+// atomic add (the combine).
+constexpr int kDnTile = 128;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_mfma_kernel(FfnArgs a, const uint8_t* __restrict__ hqc,
                                                         const uint8_t* __restrict__ hqs,
-                                                        float* __restrict__ y)
+                                                        float* __restrict__ y, float* __restrict__ o)
 {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kAStage];
+    __shared__ const uint8_t* rows_c[16 * kMT];
+    __shared__ const uint8_t* rows_s[16 * kMT];
+    const int ntiles = (a.d + kDnTile - 1) / kDnTile;
+    int slot, dtile;
+    if (!xcd_tile(blockIdx.x, a.nslots, ntiles, slot, dtile)) return;
     int e, r_beg, n_e;
-    if (!mx_slot_expert(a, blockIdx.y, e, r_beg, n_e)) return;
+    if (!mx_slot_expert(a, slot, e, r_beg, n_e)) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;
-    const int nw = blockIdx.x * 256 + wave * 64;
-    if (nw >= a.d) return;
+    const int nw = dtile * kDnTile + wave * 32;
     const int K = a.f;
     const size_t crow = (size_t)(K >> 1), srow = (size_t)(K >> 5);
-    const bool ch512 = (K % 512) == 0;
-    const uint8_t *bc[4], *bs[4];
-    bool sub_ok[4];
+    const uint8_t* bc[2];
+    const uint8_t* bs[2];
+    bool sub_ok[2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        int n = nw + 16 * s;
-        sub_ok[s] = n < a.d;
-        size_t wr = (size_t)e * a.d + (sub_ok[s] ? n : nw) + li;
+    for (int s = 0; s < 2; ++s) {
+        const int n = nw + 16 * s;
+        sub_ok[s] = n < a.d;  // d % 32 == 0: 16-row subtiles are whole
+        const size_t wr = (size_t)e * a.d + (sub_ok[s] ? n : 0) + li;
         bc[s] = a.dc + wr * crow;
         bs[s] = a.ds + wr * srow;
     }
     for (int m0 = 0; m0 < n_e; m0 += 16 * kMT) {
-        const int mt_n = min(kMT, (n_e - m0 + 15) >> 4);
-        const uint8_t *ac[kMT], *as[kMT];
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-            size_t r = (size_t)(r_beg + min(m0 + 16 * mt + li, n_e - 1));
-            ac[mt] = hqc + r * crow;
-            as[mt] = hqs + r * srow;
+        const int nrows = min(16 * kMT, n_e - m0);
+        const int mt_n = (nrows + 15) >> 4;
+        if (threadIdx.x < 16 * kMT) {
+            const size_t r = (size_t)(r_beg + min(m0 + (int)threadIdx.x, n_e - 1));
+            rows_c[threadIdx.x] = hqc + r * crow;
+            rows_s[threadIdx.x] = hqs + r * srow;
         }
-        f32x4 c[kMT][4];
+        __syncthreads();
+        f32x4 c[kMT][2];
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) c[mt][s] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        if (ch512) {
-            for (int kc = 0; kc < K; kc += 512) {
-                Frag512 fb[4];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) load_frag512(bc[s], bs[s], kc, g, fb[s]);
-#pragma unroll
-                for (int mt = 0; mt < kMT; ++mt) {
-                    if (mt < mt_n) {
-                        Frag512 fa;
-                        load_frag512(ac[mt], as[mt], kc, g, fa);
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) {
-                            c[mt][s] = mfma_fp4<0>(fa.q[0], fb[s].q[0], fa.s, fb[s].s, c[mt][s]);
-                            c[mt][s] = mfma_fp4<1>(fa.q[1], fb[s].q[1], fa.s, fb[s].s, c[mt][s]);
-                            c[mt][s] = mfma_fp4<2>(fa.q[2], fb[s].q[2], fa.s, fb[s].s, c[mt][s]);
-                            c[mt][s] = mfma_fp4<3>(fa.q[3], fb[s].q[3], fa.s, fb[s].s, c[mt][s]);
-                        }
-                    }
-                }
-            }
-        } else {
-            for (int kc = 0; kc < K; kc += 128) {
-                uint4 qb[4];
-                uint32_t sb[4];
-#pragma unroll
-                for (int s = 0; s < 4; ++s) load_frag128(bc[s], bs[s], kc, g, K, qb[s], sb[s]);
-#pragma unroll
-                for (int mt = 0; mt < kMT; ++mt) {
-                    if (mt < mt_n) {
-                        uint4 qa;
-                        uint32_t sa;
-                        load_frag128(ac[mt], as[mt], kc, g, K, qa, sa);
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) c[mt][s] = mfma_fp4<0>(qa, qb[s], sa, sb[s], c[mt][s]);
-                    }
-                }
-            }
-        }
+            for (int s = 0; s < 2; ++s) c[mt][s] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if ((K % 512) == 0)
+            gemm_pass512<2>(rows_c, rows_s, nrows, bc, bs, K, mt_n, li, g, lds, c);
+        else
+            gemm_pass128<2>(rows_c, rows_s, nrows, bc, bs, K, mt_n, li, g, c);
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
             if (mt >= mt_n) break;
@@ -404,24 +484,33 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(FfnArgs a, const uint8_t
             for (int v = 0; v < 4; ++v) {
                 const int m = m0 + 16 * mt + 4 * g + v;
                 if (m < n_e) {
-                    const int pair = a.perm_pair[r_beg + m];
-                    const int t = pair / a.k;
-                    const float w = a.topk_w[pair];
-                    float* yr = y + (size_t)t * a.d + nw + li;
+                    if (o) {
+                        // per-pair output row (grouped order); the combine kernel gathers
+                        float* orow = o + (size_t)(r_beg + m) * a.d + nw + li;
 #pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        if (sub_ok[s]) unsafeAtomicAdd(yr + 16 * s, w * c[mt][s][v]);
+                        for (int s = 0; s < 2; ++s)
+                            if (sub_ok[s]) orow[16 * s] = c[mt][s][v];
+                    } else {
+                        const int pair = a.perm_pair[r_beg + m];
+                        const int t = pair / a.k;
+                        const float w = a.topk_w[pair];
+                        float* yr = y + (size_t)t * a.d + nw + li;
+#pragma unroll
+                        for (int s = 0; s < 2; ++s)
+                            if (sub_ok[s]) unsafeAtomicAdd(yr + 16 * s, w * c[mt][s][v]);
+                    }
                 }
             }
         }
+        __syncthreads();  // rows_c / rows_s reused by the next pass
     }
 }
 
 void launch_down_mfma(const FfnArgs& a, const uint8_t* hq_codes, const uint8_t* hq_scales, float* y,
-                      hipStream_t s)
+                      float* o, hipStream_t s)
 {
-    dim3 grid((a.d + 255) / 256, a.nslots);
-    down_mfma_kernel<<<grid, dim3(256), 0, s>>>(a, hq_codes, hq_scales, y);
+    const int grid = xcd_grid(a.nslots, (a.d + kDnTile - 1) / kDnTile);
+    down_mfma_kernel<<<dim3(grid), dim3(256), 0, s>>>(a, hq_codes, hq_scales, y, o);
 }
 
 }  // namespace k3
