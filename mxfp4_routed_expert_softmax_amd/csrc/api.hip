@@ -22,6 +22,10 @@ WsLayout ws_layout(int T, int E, int k, int d, int f, int act_mode)
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
     L.logits = take((size_t)T * E * sizeof(double));
+    {
+        const int ns = router_splits(T, E, d);
+        L.partials = take(ns > 1 ? (size_t)ns * T * E * sizeof(double) : 0);
+    }
     L.chunk_masks = take(nch * E * sizeof(uint64_t));
     L.chunk_base = take(nch * E * sizeof(int32_t));
     L.active = take(((size_t)E + 1) * sizeof(int32_t));
@@ -169,7 +173,8 @@ static void enqueue_route(const k3moe_dims* dm, const float* x, const float* w_r
 {
     double* logits = reinterpret_cast<double*>(ws + L.logits);
     launch_router_logits(dm->T, dm->E, dm->d_model, x, w_router, bias,
-                         bias_mode == K3MOE_BIAS_LOGITS, logits, s);
+                         bias_mode == K3MOE_BIAS_LOGITS, logits,
+                         reinterpret_cast<double*>(ws + L.partials), s);
     launch_topk_group(dm->T, dm->E, dm->k, logits, bias, bias_mode == K3MOE_BIAS_SELECT_ONLY,
                       topk_idx, topk_w, reinterpret_cast<uint64_t*>(ws + L.chunk_masks),
                       reinterpret_cast<int32_t*>(ws + L.chunk_base), counts, offsets, perm_pair,

@@ -13,6 +13,7 @@ constexpr int kChunk = 64;
 // Workspace carve-up (byte offsets from the 256-aligned workspace base).
 struct WsLayout {
     size_t logits;       // double [T][E]            router logits (+bias)
+    size_t partials;     // double [nsplit][T][E]    split-K router partial sums
     size_t chunk_masks;  // uint64 [nch][E]          which chunk tokens chose e
     size_t chunk_base;   // int32  [nch][E]          rows of e before chunk c
     size_t active;       // int32  [E + 1]           active experts, count last
@@ -29,9 +30,11 @@ struct WsLayout {
 WsLayout ws_layout(int T, int E, int k, int d, int f, int act_mode);
 
 // ---- routing ------------------------------------------------------------
+// partials: [router_splits()][T][E] fp64 scratch (unused when it returns 1)
+int router_splits(int T, int E, int d);
 void launch_router_logits(int T, int E, int d, const float* x, const float* wr,
                           const float* bias, int bias_in_logits, double* logits,
-                          hipStream_t s);
+                          double* partials, hipStream_t s);
 // top-k + weights + per-chunk masks; for T <= 64 also the whole grouping
 void launch_topk_group(int T, int E, int k, const double* logits, const float* bias,
                        int bias_select_only, int32_t* topk_idx, float* topk_w,

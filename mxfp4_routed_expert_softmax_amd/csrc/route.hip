@@ -86,73 +86,121 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(
     }
 }
 
-// Router logits, larger T: 64 tokens x 64 experts per 256-thread block, each
-// thread a 4 x 4 register tile, K staged through LDS as fp64.
-__global__ __launch_bounds__(256) void router_gemm_kernel(
-    int T, int E, int d, const float* __restrict__ x, const float* __restrict__ wr,
-    const float* __restrict__ bias, int bias_in_logits, double* __restrict__ logits)
+// Router logits, larger T: fp64 matrix cores (V_MFMA_F64_16X16X4_F64), 64
+// tokens x 64 experts per 256-thread block (each wave a 32 x 32 corner as
+// 2 x 2 MFMA tiles), x and W_r staged through LDS as fp32 and widened at the
+// operand (exact).  Lane l supplies A[l%16][l/16] and B[l/16][l%16]; it
+// receives D[l/16 + 4v][l%16].  Small batches split K over gridDim.z; the
+// partial logits are then added in split order.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void router_mfma_kernel(int T, int E, int d, int kslice,
+                                                          const float* __restrict__ x,
+                                                          const float* __restrict__ wr,
+                                                          double* __restrict__ out)
 {
     constexpr int BK = 32;
-    __shared__ double xs[BK][64 + 1];
-    __shared__ double ws[BK][64 + 1];
-    const int tid = threadIdx.x;
+    __shared__ float xs[64][BK + 1];
+    __shared__ float ws[64][BK + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
     const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
-    const int ty = tid >> 4, tx = tid & 15;  // 16 x 16 threads, 4 x 4 outputs each
-    double acc[4][4];
+    const int kb = blockIdx.z * kslice, ke = kb + kslice;
+    f64x4 acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-    for (int k0 = 0; k0 < d; k0 += BK) {
-        // 64 rows x 32 cols of x and of wr: 2048 values each, 8 per thread
+        for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = (f64x4){0.0, 0.0, 0.0, 0.0};
+    for (int k0 = kb; k0 < ke; k0 += BK) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            int idx = tid + q * 256;
-            int r = idx >> 5, c = idx & 31;
-            int tr = t0 + r, er = e0 + r;
-            xs[c][r] = (tr < T) ? (double)x[(size_t)tr * d + k0 + c] : 0.0;
-            ws[c][r] = (er < E) ? (double)wr[(size_t)er * d + k0 + c] : 0.0;
+            const int idx = tid + q * 256;
+            const int r = idx >> 5, c = idx & 31;
+            const int tr = t0 + r, er = e0 + r;
+            xs[r][c] = (tr < T) ? x[(size_t)tr * d + k0 + c] : 0.0f;
+            ws[r][c] = (er < E) ? wr[(size_t)er * d + k0 + c] : 0.0f;
         }
         __syncthreads();
-#pragma unroll 4
-        for (int c = 0; c < BK; ++c) {
-            double a[4], b[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = xs[c][ty * 4 + i];
+        for (int kk = 0; kk < BK / 4; ++kk) {
+            const int kcol = 4 * kk + (lane >> 4);
+            double a[2], b[2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = ws[c][tx * 4 + j];
+            for (int mi = 0; mi < 2; ++mi) a[mi] = (double)xs[32 * wm + 16 * mi + (lane & 15)][kcol];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int ni = 0; ni < 2; ++ni) b[ni] = (double)ws[32 * wn + 16 * ni + (lane & 15)][kcol];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
         }
         __syncthreads();
     }
+    double* o = out + (size_t)blockIdx.z * T * E;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int t = t0 + ty * 4 + i;
-        if (t >= T) continue;
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int e = e0 + tx * 4 + j;
-            if (e >= E) continue;
-            double v = acc[i][j];
-            if (bias_in_logits) v += (double)bias[e];
-            logits[(size_t)t * E + e] = v;
-        }
-    }
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = t0 + 32 * wm + 16 * mi + (lane >> 4) + 4 * v;
+                const int e = e0 + 32 * wn + 16 * ni + (lane & 15);
+                if (t < T && e < E) o[(size_t)t * E + e] = acc[mi][ni][v];
+            }
+}
+
+// logits = sum of the nsplit partial logits, in split order (+ bias)
+__global__ __launch_bounds__(256) void router_reduce_kernel(int nsplit, long n, int E, const double* __restrict__ part,
+                                                            const float* __restrict__ bias, int bias_in_logits,
+                                                            double* __restrict__ logits)
+{
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    double v = 0.0;
+    for (int sp = 0; sp < nsplit; ++sp) v += part[(size_t)sp * n + i];
+    if (bias_in_logits) v += (double)bias[i % E];
+    logits[i] = v;
+}
+
+// bias added in place (unsplit MFMA path)
+__global__ __launch_bounds__(256) void router_bias_kernel(long n, int E, const float* __restrict__ bias,
+                                                          double* __restrict__ logits)
+{
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) logits[i] += (double)bias[i % E];
+}
+
+int router_splits(int T, int E, int d)
+{
+    if (T <= kGemvTok) return 1;
+    const int tiles = ((E + 63) / 64) * ((T + 63) / 64);
+    int ns = 1;
+    // split K while the grid is small; each slice a multiple of 32 columns
+    while (tiles * ns < 256 && ns < 16 && (d / 32) % (2 * ns) == 0) ns *= 2;
+    return ns;
 }
 
 void launch_router_logits(int T, int E, int d, const float* x, const float* wr,
                           const float* bias, int bias_in_logits, double* logits,
-                          hipStream_t s)
+                          double* partials, hipStream_t s)
 {
     if (T <= kGemvTok) {
         router_gemv_kernel<<<dim3(E), dim3(256), 0, s>>>(T, E, d, x, wr, bias, bias_in_logits,
                                                          logits);
+        return;
+    }
+    const int ns = router_splits(T, E, d);
+    const long n = (long)T * E;
+    dim3 grid((E + 63) / 64, (T + 63) / 64, ns);
+    if (ns == 1) {
+        router_mfma_kernel<<<grid, dim3(256), 0, s>>>(T, E, d, d, x, wr, logits);
+        if (bias_in_logits)
+            router_bias_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(n, E, bias, logits);
     } else {
-        router_gemm_kernel<<<dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s>>>(
-            T, E, d, x, wr, bias, bias_in_logits, logits);
+        router_mfma_kernel<<<grid, dim3(256), 0, s>>>(T, E, d, d / ns, x, wr, partials);
+        router_reduce_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(ns, n, E, partials, bias,
+                                                                                  bias_in_logits, logits);
     }
 }
 
