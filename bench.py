@@ -25,7 +25,8 @@ HBM_PEAK_GBS = 8000.0     # MI355X HBM3E
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # the kernel sources whose counters profiles/traffic.json records
 TRAFFIC_SOURCES = ["mxfp4_routed_expert_softmax_amd/csrc/" + f for f in
-                   ("gemv.hip", "mx.hip", "route.hip", "api.hip", "device_common.h", "kernels.h")]
+                   ("gemv.hip", "mx.hip", "slices.hip", "route.hip", "api.hip", "device_common.h", "kernels.h",
+                    "slices.h")]
 FFN_KERNELS = ("gateup_", "down_", "combine_", "quantize_rows", "zero_kernel", "active_list")
 MXFP4_PEAK_TFLOPS = 10100.0  # dense MXFP4 matrix peak
 

@@ -33,6 +33,9 @@ WsLayout ws_layout(int T, int E, int k, int d, int f, int act_mode)
     if (act_mode == K3MOE_ACT_FP32) {
         L.h = take(P * f * sizeof(float));
         L.o = take(P * d * sizeof(float));
+        const bool pairs = P <= (size_t)kPairMajorMax;  // the slices path is a pair-path variant
+        L.hs_codes = take(pairs ? P * kSlices * f : 0);
+        L.hs_scales = take(pairs ? P * kSlices * (f / 32) : 0);
     } else {
         L.xq_codes = take((size_t)T * d / 2);
         L.xq_scales = take((size_t)T * d / 32);
@@ -223,10 +226,16 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
     if (act_mode == K3MOE_ACT_FP32) {
         float* h = reinterpret_cast<float*>(ws + L.h);
         float* o = reinterpret_cast<float*>(ws + L.o);
-        launch_gateup_gemv(a, h, s);
-        if (pair_path) {
+        if (pair_path && use_slices_path(a)) {
+            uint8_t* hsc = reinterpret_cast<uint8_t*>(ws + L.hs_codes);
+            uint8_t* hss = reinterpret_cast<uint8_t*>(ws + L.hs_scales);
+            launch_gateup_gemv_slices(a, hsc, hss, s);
+            launch_down_slices(a, hsc, hss, y, s);
+        } else if (pair_path) {
+            launch_gateup_gemv(a, h, s);
             launch_down_gather(a, h, y, s);
         } else {
+            launch_gateup_gemv(a, h, s);
             launch_down_gemv(a, h, o, s);
             launch_combine(a, o, y, s);
         }

@@ -22,6 +22,7 @@
 // across waves through LDS in a fixed order -- deterministic sums.
 #include "device_common.h"
 #include "kernels.h"
+#include "slices.h"
 
 namespace k3 {
 
@@ -179,9 +180,12 @@ constexpr int kGuRows = 32;  // row pairs per block
 // PAIR: the pair-major variant for small batches -- block y serves pair
 // p = t*k + j alone (expert topk_idx[p], token t, h row p), no grouping.
 // 4 waves per SIMD: all four blocks a CU receives at d_model 7168 are resident at once
-template <int TCH, int BPL, bool PAIR>
+// SL (pair path only): h is written as its kSlices MX-FP8 slices (the
+// block's 32 rows are exactly one 32-value block of h) instead of fp32.
+template <int TCH, int BPL, bool PAIR, bool SL = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BPL == 1 && TCH == 1 ? 4 : 1, 8)))
-void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h)
+void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h, uint8_t* __restrict__ hs_codes = nullptr,
+                        uint8_t* __restrict__ hs_scales = nullptr)
 {
     constexpr int R = 16 / TCH, HALF = R / 2;
     __shared__ float part[TCH][4][kGuRows * 2];  // [tt][wave][gate rows | up rows]
@@ -255,6 +259,22 @@ void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h)
             }
         }
         __syncthreads();
+        if (SL) {  // PAIR, TCH == 1, npairs == 32: half-wave 0 holds one MX block of h
+            static_assert(!SL || (PAIR && TCH == 1), "slices output is a pair-path option");
+            if (tid < 32) {
+                float g = 0.f, u = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    g += part[0][w][tid];
+                    u += part[0][w][kGuRows + tid];
+                }
+                uint32_t code[kSlices], sbyte[kSlices];
+                split_block(silu_f32(g) * u, code, sbyte);
+                store_block(tid, r0 >> 5, a.f, hs_codes + (size_t)r_beg * kSlices * a.f,
+                            hs_scales + (size_t)r_beg * kSlices * (a.f >> 5), code, sbyte);
+            }
+            continue;  // one token pass: the loop ends here
+        }
         // fixed-order cross-wave sum; thread (tt, r) finishes row r of token tt
         for (int i = tid; i < TCH * npairs; i += 256) {
             const int tt = i / npairs, r = i - tt * npairs;
@@ -502,6 +522,15 @@ static void gateup_dispatch(const FfnArgs& a, float* h, hipStream_t s)
 }
 
 bool use_pair_path(const FfnArgs& a) { return a.P <= kPairMajorMax && a.f <= 8192; }
+
+void launch_gateup_gemv_slices(const FfnArgs& a, uint8_t* hs_codes, uint8_t* hs_scales, hipStream_t s)
+{
+    const dim3 grid(a.f / kGuRows, a.P);
+    if (a.d / 32 <= 256)
+        gateup_gemv_kernel<1, 1, true, true><<<grid, dim3(256), 0, s>>>(a, nullptr, hs_codes, hs_scales);
+    else
+        gateup_gemv_kernel<1, 2, true, true><<<grid, dim3(256), 0, s>>>(a, nullptr, hs_codes, hs_scales);
+}
 
 void launch_gateup_gemv(const FfnArgs& a, float* h, hipStream_t s)
 {

@@ -20,6 +20,8 @@ struct WsLayout {
     size_t route_total;  // bytes the routing calls need (a prefix of the rest)
     size_t h;            // fp32   [T*k][f]          fp32 mode: SwiGLU output
     size_t o;            // fp32   [T*k][d]          fp32 mode: per-pair down
+    size_t hs_codes;     // uint8  [T*k][6][f]       fp32 pair mode: h slices
+    size_t hs_scales;    // uint8  [T*k][6][f/32]
     size_t xq_codes;     // uint8  [T][d/2]          mx mode: MX(x)
     size_t xq_scales;    // uint8  [T][d/32]
     size_t hq_codes;     // uint8  [T*k][f/2]        mx mode: MX(h)
@@ -65,6 +67,18 @@ void launch_gateup_gemv(const FfnArgs& a, float* h, hipStream_t s);
 void launch_down_gather(const FfnArgs& a, const float* h, float* y, hipStream_t s);
 void launch_down_gemv(const FfnArgs& a, const float* h, float* o, hipStream_t s);
 void launch_combine(const FfnArgs& a, const float* o, float* y, hipStream_t s);
+
+// ---- fp32-activation pair path on the scaled matrix cores ------------------
+// h of a pair is carried as kSlices MX-FP8 (E4M3) slices (slices.h): codes
+// [P][kSlices][f] bytes, scales [P][kSlices][f/32].  Taken when the pair path
+// is (d_ff a multiple of 512, at most 2048, down scales 16-byte aligned):
+// gate/up GEMV writing h as slices, then down on the matrix cores with the
+// combine fused.
+constexpr int kSlices = 6;
+bool use_slices_path(const FfnArgs& a);
+void launch_gateup_gemv_slices(const FfnArgs& a, uint8_t* hs_codes, uint8_t* hs_scales, hipStream_t s);
+void launch_down_slices(const FfnArgs& a, const uint8_t* hs_codes, const uint8_t* hs_scales, float* y,
+                        hipStream_t s);
 
 // ---- MXFP4-activation expert path (scaled-MFMA family) --------------------
 void launch_quantize_rows(long nblocks, const float* v, uint8_t* codes, uint8_t* scales,

@@ -51,6 +51,11 @@ class LayerShape:
 
 TINY = LayerShape("tiny", d=256, f=128, E=16, k=2, layer=0)
 K3 = LayerShape("k3", d=7168, f=2048, E=896, k=16, layer=1)
+# Small layers whose d_ff is a multiple of 512 (the small-batch matrix-core
+# path): three and one 512-value chunks, fewer experts per token than waves
+# per block, an odd k.
+SMALL_F1536 = LayerShape("small_f1536", d=1024, f=1536, E=24, k=4, layer=2)
+SMALL_F512 = LayerShape("small_f512", d=512, f=512, E=12, k=3, layer=3)
 
 
 @dataclasses.dataclass(frozen=True)

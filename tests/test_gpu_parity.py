@@ -171,6 +171,31 @@ def test_tiny_mx_split_step(tiny, T):
     _check_mx_split(x, ref, dbg, y, tiny["get"], toks, sh.d, sh.f, sh.k)
 
 
+# ------------------------------------------------ small d_ff % 512 layers ---
+@pytest.fixture(scope="module", params=["small_f1536", "small_f512"])
+def small(request):
+    sh = {"small_f1536": synthdata.SMALL_F1536, "small_f512": synthdata.SMALL_F512}[request.param]
+    host = synthdata.all_experts_host(sh)
+    wr = synthdata.router_weight(sh)
+    return dict(shape=sh, host=host, dev=_to_dev_experts(host), wr=wr,
+                wr_dev=torch.from_numpy(wr).to(DEV), get=host_expert_getter(sh, host))
+
+
+@pytest.mark.parametrize("T", [1, 7, 32, 40])
+def test_small_fp32_all_tokens(small, T):
+    """T*k <= 128: gate/up GEMV writing h as MX-FP8 slices, down on the matrix
+    cores; T = 40 with k = 4 takes the grouped path."""
+    sh = small["shape"]
+    _log(f"{sh.name} fp32 T={T}")
+    x = synthdata.tokens(sh, T, first=700 + T)
+    y, route = _run(x, small["wr_dev"], small["dev"], sh.k)
+    ref = oracle.route(x, small["wr"], sh.k)
+    assert_route_equal(route, ref)
+    assert_y_close(y, oracle_y(x, ref, range(T), small["get"]))
+    y2, _ = _run(x, small["wr_dev"], small["dev"], sh.k)
+    assert np.array_equal(y, y2), "not bitwise deterministic"
+
+
 # ----------------------------------------------------------- full layer ---
 @pytest.fixture(scope="module")
 def k3layer():
