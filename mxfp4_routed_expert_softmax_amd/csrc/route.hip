@@ -30,27 +30,33 @@ __device__ __forceinline__ double shfl_xor_d(double v, int m)
     return __shfl_xor(v, m, 64);
 }
 
+// R consecutive expert rows per block: the token slice a thread loads is
+// reused for all R rows.
+template <int R>
 __global__ __launch_bounds__(256) void router_gemv_kernel(
     int T, int E, int d, const float* __restrict__ x, const float* __restrict__ wr,
     const float* __restrict__ bias, int bias_in_logits, double* __restrict__ logits)
 {
-    __shared__ double part[kGemvTok][4];
+    __shared__ double part[R][kGemvTok][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int e = blockIdx.x;
-    const float4* w4 = reinterpret_cast<const float4*>(wr + (size_t)e * d);
+    const int e0 = blockIdx.x * R;
     const int n4 = d >> 2;
-    double acc[kGemvTok];
+    double acc[R][kGemvTok];
 #pragma unroll
-    for (int t = 0; t < kGemvTok; ++t) acc[t] = 0.0;
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int t = 0; t < kGemvTok; ++t) acc[r][t] = 0.0;
     for (int base = 0; base < n4; base += 256 * kRouterPerThread) {
         // branch-free (clamped) loads; lanes past the end multiply by zero
-        float4 w[kRouterPerThread];
+        float4 w[R][kRouterPerThread];
         float live[kRouterPerThread];
 #pragma unroll
         for (int j = 0; j < kRouterPerThread; ++j) {
-            int i = base + tid + 256 * j;
-            w[j] = w4[min(i, n4 - 1)];
+            const int i = base + tid + 256 * j;
             live[j] = (i < n4) ? 1.0f : 0.0f;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                w[r][j] = reinterpret_cast<const float4*>(wr + (size_t)min(e0 + r, E - 1) * d)[min(i, n4 - 1)];
         }
 #pragma unroll
         for (int t = 0; t < kGemvTok; ++t) {
@@ -60,29 +66,38 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(
 #pragma unroll
                 for (int j = 0; j < kRouterPerThread; ++j) v[j] = x4[min(base + tid + 256 * j, n4 - 1)];
 #pragma unroll
-                for (int j = 0; j < kRouterPerThread; ++j) {
-                    const double m = (double)live[j];
-                    acc[t] = fma((double)w[j].x * m, (double)v[j].x, acc[t]);
-                    acc[t] = fma((double)w[j].y * m, (double)v[j].y, acc[t]);
-                    acc[t] = fma((double)w[j].z * m, (double)v[j].z, acc[t]);
-                    acc[t] = fma((double)w[j].w * m, (double)v[j].w, acc[t]);
+                for (int r = 0; r < R; ++r) {
+#pragma unroll
+                    for (int j = 0; j < kRouterPerThread; ++j) {
+                        const double m = (double)live[j];
+                        acc[r][t] = fma((double)w[r][j].x * m, (double)v[j].x, acc[r][t]);
+                        acc[r][t] = fma((double)w[r][j].y * m, (double)v[j].y, acc[r][t]);
+                        acc[r][t] = fma((double)w[r][j].z * m, (double)v[j].z, acc[r][t]);
+                        acc[r][t] = fma((double)w[r][j].w * m, (double)v[j].w, acc[r][t]);
+                    }
                 }
             }
         }
     }
 #pragma unroll
-    for (int t = 0; t < kGemvTok; ++t) {
-        if (t < T) {
-            double v = acc[t];
-            for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_d(v, m);
-            if (lane == 0) part[t][wave] = v;
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int t = 0; t < kGemvTok; ++t) {
+            if (t < T) {
+                double v = acc[r][t];
+                for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_d(v, m);
+                if (lane == 0) part[r][t][wave] = v;
+            }
         }
     }
     __syncthreads();
-    if (tid < T) {
-        double v = ((part[tid][0] + part[tid][1]) + part[tid][2]) + part[tid][3];
-        if (bias_in_logits) v += (double)bias[e];
-        logits[(size_t)tid * E + e] = v;
+    if (tid < R * T) {
+        const int r = tid / T, t = tid - r * T, e = e0 + r;
+        if (e < E) {
+            double v = ((part[r][t][0] + part[r][t][1]) + part[r][t][2]) + part[r][t][3];
+            if (bias_in_logits) v += (double)bias[e];
+            logits[(size_t)t * E + e] = v;
+        }
     }
 }
 
@@ -186,8 +201,11 @@ void launch_router_logits(int T, int E, int d, const float* x, const float* wr,
                           double* partials, hipStream_t s)
 {
     if (T <= kGemvTok) {
-        router_gemv_kernel<<<dim3(E), dim3(256), 0, s>>>(T, E, d, x, wr, bias, bias_in_logits,
-                                                         logits);
+        if (T <= 2 && E >= 512)  // two rows per block still leave > 256 blocks
+            router_gemv_kernel<2><<<dim3((E + 1) / 2), dim3(256), 0, s>>>(T, E, d, x, wr, bias, bias_in_logits,
+                                                                         logits);
+        else
+            router_gemv_kernel<1><<<dim3(E), dim3(256), 0, s>>>(T, E, d, x, wr, bias, bias_in_logits, logits);
         return;
     }
     const int ns = router_splits(T, E, d);
