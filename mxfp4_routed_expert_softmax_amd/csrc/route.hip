@@ -115,8 +115,10 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(int T, int E, int d, i
                                                           double* __restrict__ out)
 {
     constexpr int BK = 32;
-    __shared__ float xs[64][BK + 1];
-    __shared__ float ws[64][BK + 1];
+    // two LDS buffers: the next K step is fetched into registers while this
+    // one is on the matrix cores, then stored to the other buffer
+    __shared__ float xs[2][64][BK + 1];
+    __shared__ float ws[2][64][BK + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
     const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
@@ -126,31 +128,50 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(int T, int E, int d, i
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = (f64x4){0.0, 0.0, 0.0, 0.0};
-    for (int k0 = kb; k0 < ke; k0 += BK) {
+    float xr[8], wv[8];
+    auto fetch = [&](int k0) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int idx = tid + q * 256;
             const int r = idx >> 5, c = idx & 31;
             const int tr = t0 + r, er = e0 + r;
-            xs[r][c] = (tr < T) ? x[(size_t)tr * d + k0 + c] : 0.0f;
-            ws[r][c] = (er < E) ? wr[(size_t)er * d + k0 + c] : 0.0f;
+            xr[q] = (tr < T) ? x[(size_t)tr * d + k0 + c] : 0.0f;
+            wv[q] = (er < E) ? wr[(size_t)er * d + k0 + c] : 0.0f;
         }
-        __syncthreads();
+    };
+    auto stash = [&](int b) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int idx = tid + q * 256;
+            const int r = idx >> 5, c = idx & 31;
+            xs[b][r][c] = xr[q];
+            ws[b][r][c] = wv[q];
+        }
+    };
+    fetch(kb);
+    stash(0);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = kb; k0 < ke; k0 += BK) {
+        const bool more = k0 + BK < ke;
+        if (more) fetch(k0 + BK);
 #pragma unroll
         for (int kk = 0; kk < BK / 4; ++kk) {
             const int kcol = 4 * kk + (lane >> 4);
-            double a[2], b[2];
+            double av[2], bv[2];
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) a[mi] = (double)xs[32 * wm + 16 * mi + (lane & 15)][kcol];
+            for (int mi = 0; mi < 2; ++mi) av[mi] = (double)xs[buf][32 * wm + 16 * mi + (lane & 15)][kcol];
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni) b[ni] = (double)ws[32 * wn + 16 * ni + (lane & 15)][kcol];
+            for (int ni = 0; ni < 2; ++ni) bv[ni] = (double)ws[buf][32 * wn + 16 * ni + (lane & 15)][kcol];
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[mi], bv[ni], acc[mi][ni], 0, 0, 0);
         }
+        if (more) stash(buf ^ 1);
         __syncthreads();
+        buf ^= 1;
     }
     double* o = out + (size_t)blockIdx.z * T * E;
 #pragma unroll
