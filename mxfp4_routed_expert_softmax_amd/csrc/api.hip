@@ -257,7 +257,7 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
         launch_gateup_mfma(a, xqc, xqs, hqc, hqs, dbg ? dbg->h : nullptr,
                            dbg ? dbg->h_codes : nullptr, dbg ? dbg->h_scales : nullptr, s);
         float* o = reinterpret_cast<float*>(ws + L.o);
-        launch_down_mfma(a, hqc, hqs, y, o, s);
+        launch_down_mfma(a, hqc, hqs, o, s);
         launch_combine(a, o, y, s);
     }
     return K3MOE_OK;

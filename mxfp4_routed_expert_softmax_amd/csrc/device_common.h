@@ -85,4 +85,74 @@ __device__ __forceinline__ void load32f(const float* p, float* xs)
     }
 }
 
+// ---- buffer loads -------------------------------------------------------
+// Weight rows are read through a buffer resource on the block's (uniform)
+// matrix base: one 32-bit lane offset serves every row (the row offset is a
+// scalar), and a lane whose offset is >= 2^31 reads zeros without touching
+// memory -- the lanes past the end of the reduction axis.
+constexpr uint32_t kOff = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const uint8_t* base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 ld_codes(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, (int)soff, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint32_t ld_scale(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b8(r, voff, (int)soff, 0);
+}
+
+// ---- direct global->LDS copies (gfx950 global_load_lds_dwordx4) ---------
+// LDS byte address of a pointer into __shared__ memory (the low half of the
+// flat address; the shared aperture is 4 GiB aligned)
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)reinterpret_cast<uintptr_t>(p);
+}
+
+// One 16-byte-per-lane global->LDS copy from base + off (base wave-uniform,
+// in SGPRs; off per lane); lane l lands at LDS address m0 + 16*l.  Written as
+// assembly so that the compiler neither serialises the copies nor waits on
+// them before LDS reads: completion is awaited explicitly (vm_wait)
+// before a stage is read.  m0 is restored; one wait state separates its
+// write from the copy.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t m0)
+{
+    base = uniform_ptr(base);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(m0)
+        : "memory");
+}
+
+// Wait until at most N vector-memory loads issued by this wave are still in
+// flight (they complete in issue order).  vmcnt sits in bits [3:0] and
+// [15:14] of the immediate; expcnt (7) and lgkmcnt (15) are left free.
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 }  // namespace k3

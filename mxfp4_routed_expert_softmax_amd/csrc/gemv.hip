@@ -143,28 +143,6 @@ __device__ __forceinline__ void dot32_multi(uint4 q, float sc, const float (&xs)
     }
 }
 
-// Weight rows are read through a buffer resource on the block's (uniform)
-// matrix base: one 32-bit lane offset serves every row (the row offset is a
-// scalar), and a lane whose offset is >= 2^31 reads zeros without touching
-// memory -- the lanes past the end of the reduction axis.
-constexpr uint32_t kOff = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t weight_rsrc(const uint8_t* base)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, 0x7fffffff, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 ld_codes(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, (int)soff, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-__device__ __forceinline__ uint32_t ld_scale(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    return __builtin_amdgcn_raw_buffer_load_b8(r, voff, (int)soff, 0);
-}
-
 // ---------------------------------------------------------------------------
 // Partial sums of a batch: acc[tt * R + i] = row i of the batch for token tt,
 // R = 16 / TCH rows per batch, so one transposed reduction serves the batch.

@@ -87,9 +87,8 @@ void launch_gateup_mfma(const FfnArgs& a, const uint8_t* xq_codes, const uint8_t
                         uint8_t* hq_codes, uint8_t* hq_scales, float* dbg_h,
                         uint8_t* dbg_hc, uint8_t* dbg_hs, hipStream_t s);
 void launch_zero(float* y, size_t n, hipStream_t s);
-// o == nullptr: atomic scatter-add of w * o into y (y zeroed first);
-// else per-pair rows into o [T*k][d] (grouped order) for launch_combine
-void launch_down_mfma(const FfnArgs& a, const uint8_t* hq_codes, const uint8_t* hq_scales,
-                      float* y, float* o, hipStream_t s);
+// per-pair rows into o [T*k][d] (grouped order) for launch_combine
+void launch_down_mfma(const FfnArgs& a, const uint8_t* hq_codes, const uint8_t* hq_scales, float* o,
+                      hipStream_t s);
 
 }  // namespace k3

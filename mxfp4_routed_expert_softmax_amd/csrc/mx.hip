@@ -178,108 +178,108 @@ static int xcd_grid(int nslots, int ntiles)
 }
 
 // ---------------------------------------------------------------------------
-// Grouped scaled-MFMA GEMM building blocks.  A = activation rows of one
-// expert (x_q rows of its tokens, or its h_q rows), staged per 512-wide K
-// chunk in LDS: row m holds 256 code bytes then the chunk's 16 scale bytes
-// (272-byte stride, which also spreads rows over the LDS banks); two buffers,
-// the next chunk is fetched into registers while the current one is used.
-// B = weight rows, loaded straight into registers (each weight byte is used
-// by exactly one wave), also one chunk ahead.
-constexpr int kMT = 8;             // 16-token tiles per pass (M <= 128)
-constexpr int kARow = 272;         // LDS bytes per staged activation row
-constexpr int kAStage = 16 * kMT * kARow;
+// Epilogues shared by both GEMM forms.  Accumulator c[mt][s] of lane
+// (g, li) holds row (token) 16*mt + 4*g + v, column li of subtile s.
+constexpr int kMT = 8;  // 16-token tiles per pass (M <= 128)
 
-// Stage the A chunk kc into an LDS buffer with the gfx950 direct
-// global->LDS load (lane l of a wave instruction lands at M0 + 16*l): item
-// it = 17*r + c (16 code pieces then the scale piece of row r) goes to LDS
-// byte 16*it, i.e. row r at r*kARow.  Rows past the expert's tokens repeat its
-// last row; their outputs are discarded.
-__device__ __forceinline__ void a_issue(const uint8_t* const* rows_c, const uint8_t* const* rows_s, int nrows,
-                                        int mt_n, int kc, uint8_t* dst)
+// Eight values -> eight E2M1 codes in one word (element 2i in the low
+// nibble of byte i): the gfx950 convert rounds to nearest even and
+// saturates at 6, keeping the sign (the OCP rule above); the scale is
+// applied beforehand as an exact power-of-two product.
+__device__ __forceinline__ uint32_t e2m1_pack8(const float* v, float inv)
 {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int n_items = 16 * mt_n * 17;  // a multiple of 64 when mt_n is even; else the tail is masked
-#pragma unroll
-    for (int i = 0; i < 9; ++i) {
-        const int base = 256 * i + 64 * wave;
-        if (base >= n_items) break;
-        const int it = base + lane;
-        if (it < n_items) {
-            const int r = min(it / 17, nrows - 1), c = it - (it / 17) * 17;
-            const uint8_t* src = c < 16 ? rows_c[r] + (kc >> 1) + 16 * c : rows_s[r] + (kc >> 5);
-            __builtin_amdgcn_global_load_lds(src, dst + 16 * base, 16, 0, 0);
-        }
-    }
+    uint32_t w = 0u;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0] * inv, v[1] * inv, 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] * inv, v[3] * inv, 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4] * inv, v[5] * inv, 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6] * inv, v[7] * inv, 1.0f, 3);
+    return w;
 }
 
-// A fragment of M-tile mt for this lane (row 16*mt + li, quarter g)
-__device__ __forceinline__ void a_frag(const uint8_t* lds, int mt, int li, int g, Frag512& f)
-{
-    const uint8_t* row = lds + (16 * mt + li) * kARow;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.q[i] = *reinterpret_cast<const uint4*>(row + 64 * g + 16 * i);
-    f.s = *reinterpret_cast<const uint32_t*>(row + 256 + 4 * g);
-}
+// gate/up: h = silu(g) * u of this wave's 16 columns -> LDS hx [m][64] (row
+// stride 65 words, so that the quantiser's per-row reads fall on distinct
+// banks), then the MX quantiser over each token's 32 consecutive f values
+// (held by two neighbouring waves), one thread per (row, 32-column block).
+constexpr int kHxStride = 65;
 
-template <int NB>
-__device__ __forceinline__ void b_fetch(Frag512 (&F)[NB], const uint8_t* const (&bc)[NB],
-                                        const uint8_t* const (&bs)[NB], int kc, int g)
+template <int MT>
+__device__ __forceinline__ void gateup_epilogue(const FfnArgs& a, const f32x4 (&c)[MT][2], float* hx, int mt_n,
+                                                int nrows, int m0, int r_beg, int n0, int wave, int li, int g,
+                                                uint8_t* __restrict__ hqc, uint8_t* __restrict__ hqs,
+                                                float* __restrict__ dbg_h, uint8_t* __restrict__ dbg_hc,
+                                                uint8_t* __restrict__ dbg_hs)
 {
+    constexpr int kW = 64;  // f columns per block
 #pragma unroll
-    for (int s = 0; s < NB; ++s) load_frag512(bc[s], bs[s], kc, g, F[s]);
-}
-
-// M-tiles one at a time, the next tile's A fragment read from LDS while the
-// current one is on the matrix cores (keeps at most two fragments live)
-template <int NB>
-__device__ __forceinline__ void mma_chunk(const Frag512 (&F)[NB], const uint8_t* lds, int mt_n, int li, int g,
-                                          f32x4 (&c)[kMT][NB])
-{
-    Frag512 fa, fn;
-    a_frag(lds, 0, li, g, fa);
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
         if (mt < mt_n) {
-            if (mt + 1 < mt_n) a_frag(lds, mt + 1, li, g, fn);
 #pragma unroll
-            for (int s = 0; s < NB; ++s) {
-                c[mt][s] = mfma_fp4<0>(fa.q[0], F[s].q[0], fa.s, F[s].s, c[mt][s]);
-                c[mt][s] = mfma_fp4<1>(fa.q[1], F[s].q[1], fa.s, F[s].s, c[mt][s]);
-                c[mt][s] = mfma_fp4<2>(fa.q[2], F[s].q[2], fa.s, F[s].s, c[mt][s]);
-                c[mt][s] = mfma_fp4<3>(fa.q[3], F[s].q[3], fa.s, F[s].s, c[mt][s]);
+            for (int v = 0; v < 4; ++v) {
+                const int m = 16 * mt + 4 * g + v;
+                hx[m * kHxStride + 16 * wave + li] = silu_f32(c[mt][0][v]) * c[mt][1][v];
             }
-            fa = fn;
-            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __syncthreads();
+    for (int it = threadIdx.x; it < nrows * (kW / 32); it += 256) {
+        const int m = it >> 1, hb = it & 1;
+        const int col0 = n0 + 32 * hb;
+        if (col0 < a.f) {
+            float hv[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) hv[i] = hx[m * kHxStride + 32 * hb + i];
+            float amax = 0.f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(hv[i]));
+            const uint32_t byte = mx_scale_byte(amax);
+            const float inv = mx_inv_scale(byte);
+            const uint4 w4 = make_uint4(e2m1_pack8(hv, inv), e2m1_pack8(hv + 8, inv), e2m1_pack8(hv + 16, inv),
+                                        e2m1_pack8(hv + 24, inv));
+            const size_t r = (size_t)(r_beg + m0 + m);
+            const size_t fcb = (size_t)(a.f >> 1), fsb = (size_t)(a.f >> 5);
+            const int blk = col0 >> 5;
+            *reinterpret_cast<uint4*>(hqc + r * fcb + 16 * blk) = w4;
+            hqs[r * fsb + blk] = (uint8_t)byte;
+            if (dbg_h || dbg_hc || dbg_hs) {
+                const int pair = a.perm_pair[r];
+                if (dbg_hc) *reinterpret_cast<uint4*>(dbg_hc + (size_t)pair * fcb + 16 * blk) = w4;
+                if (dbg_hs) dbg_hs[(size_t)pair * fsb + blk] = (uint8_t)byte;
+                if (dbg_h) {
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) dbg_h[(size_t)pair * a.f + col0 + i] = hv[i];
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// down: per-pair fp32 rows o (grouped order) for the deterministic combine;
+// subtile s of this wave covers d rows nw + 16*s .. +15
+template <int MT>
+__device__ __forceinline__ void down_epilogue(const FfnArgs& a, const f32x4 (&c)[MT][2], int mt_n, int m0,
+                                              int n_e, int r_beg, int nw, const bool (&sub_ok)[2], int li, int g,
+                                              float* __restrict__ o)
+{
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        if (mt >= mt_n) break;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = m0 + 16 * mt + 4 * g + v;
+            if (m < n_e) {
+                float* orow = o + (size_t)(r_beg + m) * a.d + nw + li;
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    if (sub_ok[s]) orow[16 * s] = c[mt][s][v];
+            }
         }
     }
 }
 
-// The K loop of one M pass (K % 512 == 0): LDS double buffer for A filled by
-// DMA one chunk ahead; the B fragments of a chunk are loaded at its start
-// (their latency overlaps the other resident waves' matrix work).
-template <int NB>
-__device__ __forceinline__ void gemm_pass512(const uint8_t* const* rows_c, const uint8_t* const* rows_s, int nrows,
-                                             const uint8_t* const (&bc)[NB], const uint8_t* const (&bs)[NB],
-                                             int K, int mt_n, int li, int g, uint8_t* lds, f32x4 (&c)[kMT][NB])
-{
-    Frag512 F[NB];
-    a_issue(rows_c, rows_s, nrows, mt_n, 0, lds);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    int buf = 0;
-    for (int kc = 0; kc < K; kc += 512) {
-        b_fetch<NB>(F, bc, bs, kc, g);
-        const bool more = kc + 512 < K;
-        if (more) a_issue(rows_c, rows_s, nrows, mt_n, kc + 512, lds + (buf ^ 1) * kAStage);
-        mma_chunk<NB>(F, lds + buf * kAStage, mt_n, li, g, c);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();  // next buffer landed; every wave is done with this one
-        buf ^= 1;
-    }
-}
-
-// 128-wide K steps for reduction axes that are not a multiple of 512 (small
-// layers); A straight from global memory.
+// ---------------------------------------------------------------------------
+// Any K (a multiple of 32; the small layers): 128-wide K steps, both
+// operands straight from global memory, zeros past the row end.
 template <int NB>
 __device__ __forceinline__ void gemm_pass128(const uint8_t* const* rows_c, const uint8_t* const* rows_s, int nrows,
                                              const uint8_t* const (&bc)[NB], const uint8_t* const (&bs)[NB],
@@ -304,15 +304,11 @@ __device__ __forceinline__ void gemm_pass128(const uint8_t* const* rows_c, const
     }
 }
 
-// ---------------------------------------------------------------------------
 // gate/up GEMM: block = 4 waves, n-tile = 64 f rows; wave w owns gate rows
 // and up rows [n0 + 16w, +16).  M = the expert's tokens, up to 128 per pass.
-// Epilogue: h = silu(g) * u in fp32; the MX quantiser runs over each token's
-// 32 consecutive f values, held by two neighbouring waves' subtiles, so the
-// block exchanges h through LDS once per pass.
 constexpr int kGuTile = 64;
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_mfma_kernel(FfnArgs a, const uint8_t* __restrict__ xqc,
+__global__ __launch_bounds__(256) void gateup_mfma_kernel(FfnArgs a, const uint8_t* __restrict__ xqc,
                                                           const uint8_t* __restrict__ xqs,
                                                           uint8_t* __restrict__ hqc,
                                                           uint8_t* __restrict__ hqs,
@@ -320,7 +316,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                           uint8_t* __restrict__ dbg_hc,
                                                           uint8_t* __restrict__ dbg_hs)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kAStage];
+    __shared__ float hx[16 * kMT * kHxStride];
     __shared__ const uint8_t* rows_c[16 * kMT];
     __shared__ const uint8_t* rows_s[16 * kMT];
     const int ntiles = (a.f + kGuTile - 1) / kGuTile;
@@ -343,7 +339,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         bc[1] = a.uc + wr * crow;
         bs[1] = a.us + wr * srow;
     }
-    float* hx = reinterpret_cast<float*>(lds);  // h exchange after the K loop: [128][64] fp32 = 32 KB
     for (int m0 = 0; m0 < n_e; m0 += 16 * kMT) {
         const int nrows = min(16 * kMT, n_e - m0);
         const int mt_n = (nrows + 15) >> 4;
@@ -360,82 +355,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             c[mt][0] = (f32x4){0.f, 0.f, 0.f, 0.f};
             c[mt][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
-        if ((K % 512) == 0)
-            gemm_pass512<2>(rows_c, rows_s, nrows, bc, bs, K, mt_n, li, g, lds, c);
-        else
-            gemm_pass128<2>(rows_c, rows_s, nrows, bc, bs, K, mt_n, li, g, c);
-        // h of this wave's 16 columns -> LDS [m][16*wave + col]
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-            if (mt < mt_n) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int m = 16 * mt + 4 * g + v;
-                    hx[m * kGuTile + 16 * wave + li] = silu_f32(c[mt][0][v]) * c[mt][1][v];
-                }
-            }
-        }
-        __syncthreads();
-        // quantise: one thread per (token row, 32-column block): 128 x 2 items
-        for (int it = threadIdx.x; it < nrows * (kGuTile / 32); it += 256) {
-            const int m = it >> 1, hb = it & 1;
-            const int col0 = n0 + 32 * hb;
-            if (col0 < a.f) {
-                const float* hv = hx + m * kGuTile + 32 * hb;
-                float amax = 0.f;
-#pragma unroll
-                for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(hv[i]));
-                const uint32_t byte = mx_scale_byte(amax);
-                const float inv = mx_inv_scale(byte);
-                uint32_t w4[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint32_t wv = 0;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) wv |= e2m1_encode(hv[8 * q + i], inv) << (4 * i);
-                    w4[q] = wv;
-                }
-                const size_t r = (size_t)(r_beg + m0 + m);
-                const size_t fcb = (size_t)(a.f >> 1), fsb = (size_t)(a.f >> 5);
-                const int blk = col0 >> 5;
-                *reinterpret_cast<uint4*>(hqc + r * fcb + 16 * blk) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-                hqs[r * fsb + blk] = (uint8_t)byte;
-                if (dbg_h || dbg_hc || dbg_hs) {
-                    const int pair = a.perm_pair[r];
-                    if (dbg_hc) *reinterpret_cast<uint4*>(dbg_hc + (size_t)pair * fcb + 16 * blk) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-                    if (dbg_hs) dbg_hs[(size_t)pair * fsb + blk] = (uint8_t)byte;
-                    if (dbg_h) {
-#pragma unroll
-                        for (int i = 0; i < 32; ++i) dbg_h[(size_t)pair * a.f + col0 + i] = hv[i];
-                    }
-                }
-            }
-        }
-        __syncthreads();
+        gemm_pass128<2>(rows_c, rows_s, nrows, bc, bs, K, mt_n, li, g, c);
+        gateup_epilogue<kMT>(a, c, hx, mt_n, nrows, m0, r_beg, n0, wave, li, g, hqc, hqs, dbg_h, dbg_hc, dbg_hs);
     }
 }
 
-void launch_gateup_mfma(const FfnArgs& a, const uint8_t* xq_codes, const uint8_t* xq_scales,
-                        uint8_t* hq_codes, uint8_t* hq_scales, float* dbg_h, uint8_t* dbg_hc,
-                        uint8_t* dbg_hs, hipStream_t s)
-{
-    const int grid = xcd_grid(a.nslots, (a.f + kGuTile - 1) / kGuTile);
-    gateup_mfma_kernel<<<dim3(grid), dim3(256), 0, s>>>(a, xq_codes, xq_scales, hq_codes, hq_scales, dbg_h,
-                                                        dbg_hc, dbg_hs);
-}
-
-// ---------------------------------------------------------------------------
 // down GEMM: block = 4 waves, n-tile = 128 d rows; wave w owns rows
 // [n0 + 32w, +32) as two 16-row subtiles; A = the expert's h_q rows
-// (contiguous in grouped order).  Epilogue: y[t][c] += w[t,j] * o[c], fp32
-// atomic add (the combine).
+// (contiguous in grouped order).
 constexpr int kDnTile = 128;
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_mfma_kernel(FfnArgs a, const uint8_t* __restrict__ hqc,
-                                                        const uint8_t* __restrict__ hqs,
-                                                        float* __restrict__ y, float* __restrict__ o)
+__global__ __launch_bounds__(256) void down_mfma_kernel(FfnArgs a, const uint8_t* __restrict__ hqc,
+                                                        const uint8_t* __restrict__ hqs, float* __restrict__ o)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kAStage];
     __shared__ const uint8_t* rows_c[16 * kMT];
     __shared__ const uint8_t* rows_s[16 * kMT];
     const int ntiles = (a.d + kDnTile - 1) / kDnTile;
@@ -473,44 +405,367 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
             for (int s = 0; s < 2; ++s) c[mt][s] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        if ((K % 512) == 0)
-            gemm_pass512<2>(rows_c, rows_s, nrows, bc, bs, K, mt_n, li, g, lds, c);
-        else
-            gemm_pass128<2>(rows_c, rows_s, nrows, bc, bs, K, mt_n, li, g, c);
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-            if (mt >= mt_n) break;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int m = m0 + 16 * mt + 4 * g + v;
-                if (m < n_e) {
-                    if (o) {
-                        // per-pair output row (grouped order); the combine kernel gathers
-                        float* orow = o + (size_t)(r_beg + m) * a.d + nw + li;
-#pragma unroll
-                        for (int s = 0; s < 2; ++s)
-                            if (sub_ok[s]) orow[16 * s] = c[mt][s][v];
-                    } else {
-                        const int pair = a.perm_pair[r_beg + m];
-                        const int t = pair / a.k;
-                        const float w = a.topk_w[pair];
-                        float* yr = y + (size_t)t * a.d + nw + li;
-#pragma unroll
-                        for (int s = 0; s < 2; ++s)
-                            if (sub_ok[s]) unsafeAtomicAdd(yr + 16 * s, w * c[mt][s][v]);
-                    }
-                }
-            }
-        }
+        gemm_pass128<2>(rows_c, rows_s, nrows, bc, bs, K, mt_n, li, g, c);
+        down_epilogue<kMT>(a, c, mt_n, m0, n_e, r_beg, nw, sub_ok, li, g, o);
         __syncthreads();  // rows_c / rows_s reused by the next pass
     }
 }
 
-void launch_down_mfma(const FfnArgs& a, const uint8_t* hq_codes, const uint8_t* hq_scales, float* y,
-                      float* o, hipStream_t s)
+// ---------------------------------------------------------------------------
+// K % 512 == 0 (the layer's d_model and d_ff): a pipelined form.
+//
+// A = the expert's activation rows (x_q rows of its tokens, or its h_q
+// rows), copied per 512-wide K chunk into LDS by direct global->LDS copies;
+// two stages, chunk i+1 is copied while chunk i is used.  Stage layout (up to
+// 96 rows): row r's 16 code pieces of 16 bytes at 256*r + 16*(p ^ (r & 15))
+// -- the XOR puts the 16 rows of one fragment read on distinct LDS banks --
+// then the rows' 16 chunk scale bytes at kACodes + 16*r.
+//
+// B = weight rows.  Their codes are buffer-loaded straight into registers
+// (each byte is used by exactly one wave) one chunk ahead of the matrix
+// work; their E8M0 scales -- 16 bytes per row and chunk, which as separate
+// loads would cost as many cache-line requests as the codes -- are copied
+// into LDS once per block (the block's rows are contiguous, so the copy is
+// one contiguous run per weight matrix) and read from there.
+constexpr int kPassMT = 6;  // 16-token tiles per pass (the register budget of two blocks per CU)
+constexpr int kACodes = 256 * 16 * kPassMT;
+constexpr int kAStage = kACodes + 16 * 16 * kPassMT;
+constexpr int kBLoads = 8;          // B code loads per chunk (two subtiles x 4)
+constexpr int kBScaleBytes = 28672; // LDS for the block's weight scales: 128 rows x K/32 (K <= 7168)
+constexpr int kMxLds = 2 * kAStage + kBScaleBytes;
+
+// Weight codes of one wave's two 16-row subtiles: buffer resources on the
+// subtiles' first rows and a per-lane offset (row li, quarter g); the
+// lane's scale words are at LDS offset bso[s] + kc/32.
+struct BSrc {
+    __amdgpu_buffer_rsrc_t rc[2];
+    uint32_t voc;
+    uint32_t bso[2];
+};
+
+__device__ __forceinline__ void b_fetch(const BSrc& b, int kc, Frag512 (&F)[2])
+{
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) F[s].q[i] = ld_codes(b.rc[s], b.voc + 16u * i, (uint32_t)(kc >> 1));
+    }
+}
+
+// Copy nbytes (a multiple of 1 KiB) of contiguous global memory to LDS dst:
+// the block's copies of 1 KiB go round-robin to its four waves.
+__device__ __forceinline__ void lds_copy(const uint8_t* src, uint32_t dst, int nbytes)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int j = wave; 1024 * j < nbytes; j += 4)
+        dma16(src + 1024 * j, 16u * (uint32_t)lane, dst + 1024u * (uint32_t)j);
+}
+
+// Per-thread copy offsets of the A stage, fixed over the K loop: code copy q
+// of wave w moves rows 4*(4q+w) .. +3, one 16-byte piece per lane; wave 0
+// copies the scale pieces of rows 0..63, wave 1 those of rows 64..95.  Rows
+// past the expert's tokens repeat its last row (their outputs are discarded).
+struct ASrc {
+    uint32_t oc[kPassMT], os;
+};
+
+__device__ __forceinline__ void a_offsets(const uint32_t* rowtok, int nrows, uint32_t crow, uint32_t srow, ASrc& A)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < kPassMT; ++q) {
+        const int r = 4 * (4 * q + wave) + (lane >> 4), p = lane & 15;
+        A.oc[q] = rowtok[min(r, nrows - 1)] * crow + 16u * (uint32_t)(p ^ (r & 15));
+    }
+    A.os = rowtok[min(64 * (wave & 1) + lane, nrows - 1)] * srow;
+}
+
+// Copy A chunk kc into an LDS stage (assembly copies, awaited explicitly)
+__device__ __forceinline__ void a_issue(const ASrc& A, const uint8_t* cbase, const uint8_t* sbase, int kc,
+                                        uint32_t dst)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint8_t* cb = cbase + (kc >> 1);
+#pragma unroll
+    for (int q = 0; q < kPassMT; ++q) dma16(cb, A.oc[q], dst + 1024u * (uint32_t)(4 * q + wave));
+    if (wave < 2 && 64 * wave + lane < 16 * kPassMT)
+        dma16(sbase + (kc >> 5), A.os, dst + (uint32_t)kACodes + 1024u * (uint32_t)wave);
+}
+
+// This lane's LDS read offsets within a stage for M-tile 0: code pieces
+// 4g+i of row li (XOR-swizzled) and the scale word of quarter g; tile mt adds
+// 4096*mt (256*mt for the scales) -- immediate offsets of the LDS reads.
+struct AOffs {
+    uint32_t q[4], s;
+};
+
+__device__ __forceinline__ AOffs a_read_offsets(int li, int g)
+{
+    AOffs o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.q[i] = (uint32_t)(256 * li + 16 * ((4 * g + i) ^ li));
+    o.s = (uint32_t)(kACodes + 16 * li + 4 * g);
+    return o;
+}
+
+// A fragment of M-tile MT_ (row 16*MT_ + li, quarter g) from stage st
+template <int MT_>
+__device__ __forceinline__ void a_frag(const uint8_t* st, const AOffs& o, Frag512& f)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.q[i] = *reinterpret_cast<const uint4*>(st + o.q[i] + 4096 * MT_);
+    f.s = *reinterpret_cast<const uint32_t*>(st + o.s + 256 * MT_);
+}
+
+template <int MT_, int MT>
+__device__ __forceinline__ void mma_tiles(const Frag512 (&F)[2], const uint32_t (&sb)[2], const uint8_t* st,
+                                          const AOffs& o, const Frag512& fa, f32x4 (&c)[MT][2])
+{
+    Frag512 fn;
+    if constexpr (MT_ + 1 < MT) a_frag<MT_ + 1>(st, o, fn);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        c[MT_][s] = mfma_fp4<0>(fa.q[0], F[s].q[0], fa.s, sb[s], c[MT_][s]);
+        c[MT_][s] = mfma_fp4<1>(fa.q[1], F[s].q[1], fa.s, sb[s], c[MT_][s]);
+        c[MT_][s] = mfma_fp4<2>(fa.q[2], F[s].q[2], fa.s, sb[s], c[MT_][s]);
+        c[MT_][s] = mfma_fp4<3>(fa.q[3], F[s].q[3], fa.s, sb[s], c[MT_][s]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MT_ + 1 < MT) mma_tiles<MT_ + 1, MT>(F, sb, st, o, fn, c);
+}
+
+// The MT M-tiles of chunk kc from stage st, one at a time, the next tile's A
+// fragment read from LDS while the current one is on the matrix cores
+template <int MT>
+__device__ __forceinline__ void mma_chunk(const Frag512 (&F)[2], const BSrc& B, const uint8_t* lds, int kc,
+                                          const uint8_t* st, const AOffs& o, f32x4 (&c)[MT][2])
+{
+    const uint8_t* bsc = lds + 2 * kAStage + (kc >> 5);
+    const uint32_t sb[2] = {*reinterpret_cast<const uint32_t*>(bsc + B.bso[0]),
+                            *reinterpret_cast<const uint32_t*>(bsc + B.bso[1])};
+    Frag512 fa;
+    a_frag<0>(st, o, fa);
+    mma_tiles<0, MT>(F, sb, st, o, fa, c);
+    // keep the matrix work here: without a use, the compiler may sink it
+    // past the copies and the barrier that follow
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        asm volatile("" : "+v"(c[mt][0]));
+        asm volatile("" : "+v"(c[mt][1]));
+    }
+}
+
+// Chunk i < nk-1, its A stage BUF = i & 1: fetch B chunk i+1 into Fn; wait
+// until only those loads are in flight (B chunk i, and every copy issued
+// before it -- the A copy of chunk i -- have landed); barrier (every wave's
+// part of A chunk i is visible, and every wave is done with the other stage);
+// copy A chunk i+1 into the other stage; run chunk i.  B is in flight one
+// chunk ahead, about two chunks of every wave's weight stream at the wait.
+template <int BUF, int MT>
+__device__ __forceinline__ void gemm_step(const ASrc& A, const BSrc& B, const uint8_t* cbase, const uint8_t* sbase,
+                                          int i, const AOffs& o, uint8_t* lds, const Frag512 (&Fc)[2],
+                                          Frag512 (&Fn)[2], f32x4 (&c)[MT][2])
+{
+    b_fetch(B, 512 * (i + 1), Fn);
+    __builtin_amdgcn_sched_barrier(0);
+    vm_wait<kBLoads>();
+    __syncthreads();
+    a_issue(A, cbase, sbase, 512 * (i + 1), lds_addr(lds) + (uint32_t)((BUF ^ 1) * kAStage));
+    __builtin_amdgcn_sched_barrier(0);
+    mma_chunk<MT>(Fc, B, lds, 512 * i, lds + BUF * kAStage, o, c);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// the last chunk: nothing left to fetch; the closing barrier frees the LDS
+// for the epilogue
+template <int BUF, int MT>
+__device__ __forceinline__ void gemm_last(const BSrc& B, int i, const AOffs& o, uint8_t* lds,
+                                          const Frag512 (&Fc)[2], f32x4 (&c)[MT][2])
+{
+    vm_wait<0>();
+    __syncthreads();
+    mma_chunk<MT>(Fc, B, lds, 512 * i, lds + BUF * kAStage, o, c);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+}
+
+// One M pass of MT tiles over the whole K axis (nk = K/512 chunks): two B
+// register sets and the two A stages swap roles every chunk (the loop body
+// holds two chunks, so no register copies).  On entry every wave has issued
+// the copies the first chunk needs (weight scales, if this is the block's
+// first pass); they land before the first wait returns.
+template <int MT>
+__device__ __forceinline__ void gemm_pass512(const ASrc& A, const BSrc& B, const uint8_t* cbase,
+                                             const uint8_t* sbase, int K, const AOffs& o, uint8_t* lds,
+                                             f32x4 (&c)[MT][2])
+{
+    const int nk = K >> 9;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        c[mt][0] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        c[mt][1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    Frag512 F0[2], F1[2];
+    a_issue(A, cbase, sbase, 0, lds_addr(lds));
+    b_fetch(B, 0, F0);
+    __builtin_amdgcn_sched_barrier(0);
+    int i = 0;
+    for (; i + 1 < nk; i += 2) {
+        gemm_step<0, MT>(A, B, cbase, sbase, i, o, lds, F0, F1, c);
+        if (i + 2 >= nk) {
+            gemm_last<1, MT>(B, i + 1, o, lds, F1, c);
+            return;
+        }
+        gemm_step<1, MT>(A, B, cbase, sbase, i + 1, o, lds, F1, F0, c);
+    }
+    gemm_last<0, MT>(B, i, o, lds, F0, c);
+}
+
+template <int MT>
+__device__ __forceinline__ void gateup_pass(const FfnArgs& a, const ASrc& A, const BSrc& B, const uint8_t* xqc,
+                                            const uint8_t* xqs, int mt_n, int nrows, int m0, int r_beg, int n0,
+                                            int wave, int li, int g, uint8_t* lds, uint8_t* hqc, uint8_t* hqs,
+                                            float* dbg_h, uint8_t* dbg_hc, uint8_t* dbg_hs)
+{
+    f32x4 c[MT][2];
+    gemm_pass512<MT>(A, B, xqc, xqs, a.d, a_read_offsets(li, g), lds, c);
+    gateup_epilogue<MT>(a, c, reinterpret_cast<float*>(lds), mt_n, nrows, m0, r_beg, n0, wave, li, g, hqc, hqs,
+                        dbg_h, dbg_hc, dbg_hs);
+}
+
+template <int MT>
+__device__ __forceinline__ void down_pass(const FfnArgs& a, const ASrc& A, const BSrc& B, const uint8_t* cbase,
+                                          const uint8_t* sbase, int mt_n, int m0, int n_e, int r_beg, int nw,
+                                          const bool (&sub_ok)[2], int li, int g, uint8_t* lds, float* o)
+{
+    f32x4 c[MT][2];
+    gemm_pass512<MT>(A, B, cbase, sbase, a.f, a_read_offsets(li, g), lds, c);
+    down_epilogue<MT>(a, c, mt_n, m0, n_e, r_beg, nw, sub_ok, li, g, o);
+}
+
+// Every pass runs kPassMT tiles (a fixed set of accumulator registers;
+// tiles past the pass's rows compute on repeated rows and are discarded).
+// Shapes: d_model and d_ff multiples of 512 and at most 7168 (the weight
+// scales of a block fit the LDS), d_ff a multiple of 64 (whole gate/up
+// tiles) and d_model a multiple of 128 (whole down tiles).
+bool use_mx512(const FfnArgs& a)
+{
+    return a.d % 512 == 0 && a.f % 512 == 0 && a.d <= 7168 && a.f <= 7168 && a.f % kGuTile == 0 &&
+           a.d % kDnTile == 0;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_mx512_kernel(
+    FfnArgs a, const uint8_t* __restrict__ xqc, const uint8_t* __restrict__ xqs, uint8_t* __restrict__ hqc,
+    uint8_t* __restrict__ hqs, float* __restrict__ dbg_h, uint8_t* __restrict__ dbg_hc,
+    uint8_t* __restrict__ dbg_hs)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMxLds];
+    __shared__ uint32_t rowtok[16 * kPassMT];
+    const int ntiles = a.f / kGuTile;
+    int slot, ftile;
+    if (!xcd_tile(blockIdx.x, a.nslots, ntiles, slot, ftile)) return;
+    int e, r_beg, n_e;
+    if (!mx_slot_expert(a, slot, e, r_beg, n_e)) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int li = lane & 15, g = lane >> 4;
+    const int n0 = ftile * kGuTile;
+    const uint32_t crow = (uint32_t)(a.d >> 1), srow = (uint32_t)(a.d >> 5);
+    // the block's weight scales: gate rows n0.. (64 rows), then up rows
+    {
+        const size_t r0 = (size_t)e * a.f + n0;
+        const int nb = kGuTile * (int)srow;
+        lds_copy(a.gs + r0 * srow, lds_addr(lds) + 2u * kAStage, nb);
+        lds_copy(a.us + r0 * srow, lds_addr(lds) + 2u * kAStage + (uint32_t)nb, nb);
+    }
+    BSrc B;
+    {
+        const size_t wr = (size_t)e * a.f + (size_t)(n0 + 16 * wave);
+        B.rc[0] = weight_rsrc(a.gc + wr * crow);
+        B.rc[1] = weight_rsrc(a.uc + wr * crow);
+        B.voc = (uint32_t)li * crow + 64u * (uint32_t)g;
+        B.bso[0] = (uint32_t)(16 * wave + li) * srow + 4u * (uint32_t)g;
+        B.bso[1] = B.bso[0] + (uint32_t)kGuTile * srow;
+    }
+    const int tiles = (n_e + 15) >> 4, npass = (tiles + kPassMT - 1) / kPassMT;
+    for (int p = 0; p < npass; ++p) {
+        // passes of near-equal tile counts (<= kPassMT)
+        const int t0 = p * tiles / npass, t1 = (p + 1) * tiles / npass;
+        const int m0 = 16 * t0, nrows = min(16 * t1, n_e) - m0, mt_n = t1 - t0;
+        if (threadIdx.x < 16 * kPassMT) {
+            const int m = m0 + min((int)threadIdx.x, nrows - 1);
+            rowtok[threadIdx.x] = (uint32_t)(a.perm_pair[r_beg + m] / a.k);
+        }
+        __syncthreads();
+        ASrc A;
+        a_offsets(rowtok, nrows, crow, srow, A);
+        gateup_pass<kPassMT>(a, A, B, xqc, xqs, mt_n, nrows, m0, r_beg, n0, wave, li, g, lds, hqc, hqs, dbg_h,
+                             dbg_hc, dbg_hs);
+    }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_mx512_kernel(
+    FfnArgs a, const uint8_t* __restrict__ hqc, const uint8_t* __restrict__ hqs, float* __restrict__ o)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMxLds];
+    __shared__ uint32_t rowtok[16 * kPassMT];
+    const int ntiles = a.d / kDnTile;
+    int slot, dtile;
+    if (!xcd_tile(blockIdx.x, a.nslots, ntiles, slot, dtile)) return;
+    int e, r_beg, n_e;
+    if (!mx_slot_expert(a, slot, e, r_beg, n_e)) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int li = lane & 15, g = lane >> 4;
+    const int nw = dtile * kDnTile + wave * 32;
+    const uint32_t crow = (uint32_t)(a.f >> 1), srow = (uint32_t)(a.f >> 5);
+    // the block's weight scales: d rows dtile*128 .. +127
+    lds_copy(a.ds + ((size_t)e * a.d + (size_t)dtile * kDnTile) * srow, lds_addr(lds) + 2u * kAStage,
+             kDnTile * (int)srow);
+    const bool sub_ok[2] = {true, true};  // d % 128 == 0
+    BSrc B;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const size_t wr = (size_t)e * a.d + (size_t)(nw + 16 * s);
+        B.rc[s] = weight_rsrc(a.dc + wr * crow);
+        B.bso[s] = (uint32_t)(32 * wave + 16 * s + li) * srow + 4u * (uint32_t)g;
+    }
+    B.voc = (uint32_t)li * crow + 64u * (uint32_t)g;
+    // h_q rows of the expert are contiguous: the copy bases start at its first row
+    const uint8_t* cbase = hqc + (size_t)r_beg * crow;
+    const uint8_t* sbase = hqs + (size_t)r_beg * srow;
+    const int tiles = (n_e + 15) >> 4, npass = (tiles + kPassMT - 1) / kPassMT;
+    for (int p = 0; p < npass; ++p) {
+        const int t0 = p * tiles / npass, t1 = (p + 1) * tiles / npass;
+        const int m0 = 16 * t0, nrows = min(16 * t1, n_e) - m0, mt_n = t1 - t0;
+        if (threadIdx.x < 16 * kPassMT) rowtok[threadIdx.x] = (uint32_t)(m0 + min((int)threadIdx.x, nrows - 1));
+        __syncthreads();
+        ASrc A;
+        a_offsets(rowtok, nrows, crow, srow, A);
+        down_pass<kPassMT>(a, A, B, cbase, sbase, mt_n, m0, n_e, r_beg, nw, sub_ok, li, g, lds, o);
+        __syncthreads();  // rowtok reused by the next pass
+    }
+}
+
+void launch_gateup_mfma(const FfnArgs& a, const uint8_t* xq_codes, const uint8_t* xq_scales,
+                        uint8_t* hq_codes, uint8_t* hq_scales, float* dbg_h, uint8_t* dbg_hc,
+                        uint8_t* dbg_hs, hipStream_t s)
+{
+    const int grid = xcd_grid(a.nslots, (a.f + kGuTile - 1) / kGuTile);
+    if (use_mx512(a))
+        gateup_mx512_kernel<<<dim3(grid), dim3(256), 0, s>>>(a, xq_codes, xq_scales, hq_codes, hq_scales, dbg_h,
+                                                             dbg_hc, dbg_hs);
+    else
+        gateup_mfma_kernel<<<dim3(grid), dim3(256), 0, s>>>(a, xq_codes, xq_scales, hq_codes, hq_scales, dbg_h,
+                                                            dbg_hc, dbg_hs);
+}
+
+void launch_down_mfma(const FfnArgs& a, const uint8_t* hq_codes, const uint8_t* hq_scales, float* o,
+                      hipStream_t s)
 {
     const int grid = xcd_grid(a.nslots, (a.d + kDnTile - 1) / kDnTile);
-    down_mfma_kernel<<<dim3(grid), dim3(256), 0, s>>>(a, hq_codes, hq_scales, y, o);
+    if (use_mx512(a))
+        down_mx512_kernel<<<dim3(grid), dim3(256), 0, s>>>(a, hq_codes, hq_scales, o);
+    else
+        down_mfma_kernel<<<dim3(grid), dim3(256), 0, s>>>(a, hq_codes, hq_scales, o);
 }
 
 }  // namespace k3

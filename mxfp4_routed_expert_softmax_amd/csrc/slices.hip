@@ -83,42 +83,6 @@ __device__ __forceinline__ f32x4 mma_chunk(const AFrag& a, const BFrag& b, f32x4
 constexpr int kStage = 4096 + 256;
 constexpr int kStageLoads = 5;  // load instructions per stage (4 code + 1 scale)
 
-// LDS byte address of a pointer into __shared__ memory (the low half of the
-// flat address; the shared aperture is 4 GiB aligned)
-__device__ __forceinline__ uint32_t lds_addr(const void* p)
-{
-    return (uint32_t)reinterpret_cast<uintptr_t>(p);
-}
-
-// One 16-byte-per-lane global->LDS copy from base + off (base wave-uniform,
-// in SGPRs; off per lane); lane l lands at LDS address m0 + 16*l.  Written as
-// assembly so that the compiler neither serialises the copies nor waits on
-// them before LDS reads: completion is awaited explicitly (wait_stages)
-// before a stage is read.  m0 is restored; one wait state separates its
-// write from the copy.
-__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p)
-{
-    const uint64_t v = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
-}
-
-__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_t m0)
-{
-    base = uniform_ptr(base);
-    m0 = __builtin_amdgcn_readfirstlane(m0);
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(off), "s"(base), "s"(m0)
-        : "memory");
-}
-
 // Per-lane offsets of a tile-chunk copy (tile rows past rmax repeat row rmax,
 // their results are discarded): code pieces j = 0..3 and the scale piece.
 struct TileOffs {
@@ -255,13 +219,10 @@ __device__ __forceinline__ void stage_bfrag(uint32_t st, int g, int i, BFrag& b)
 // between only make the wait stricter).
 __device__ __forceinline__ void wait_stages(int n)
 {
-    // vmcnt lives in bits [3:0] and [15:14]; expcnt (7) and lgkmcnt (15) are left unconstrained
-#define K3_VMCNT(N) ((((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14)))
-    if (n >= 3) __builtin_amdgcn_s_waitcnt(K3_VMCNT(3 * kStageLoads));
-    else if (n == 2) __builtin_amdgcn_s_waitcnt(K3_VMCNT(2 * kStageLoads));
-    else if (n == 1) __builtin_amdgcn_s_waitcnt(K3_VMCNT(kStageLoads));
-    else __builtin_amdgcn_s_waitcnt(K3_VMCNT(0));
-#undef K3_VMCNT
+    if (n >= 3) vm_wait<3 * kStageLoads>();
+    else if (n == 2) vm_wait<2 * kStageLoads>();
+    else if (n == 1) vm_wait<kStageLoads>();
+    else vm_wait<0>();
 }
 
 }  // namespace

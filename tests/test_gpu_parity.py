@@ -196,6 +196,23 @@ def test_small_fp32_all_tokens(small, T):
     assert np.array_equal(y, y2), "not bitwise deterministic"
 
 
+@pytest.mark.parametrize("T", [1, 37, 600])
+def test_small_mx_split_step(small, T):
+    """MXFP4 activations on layers whose d_model and d_ff are multiples of
+    512: the pipelined grouped GEMMs with one, two and three K chunks (512,
+    1024, 1536); T = 600 puts more than 96 tokens on an expert (several
+    passes per block)."""
+    sh = small["shape"]
+    _log(f"{sh.name} mx T={T}")
+    x = synthdata.tokens(sh, T, first=9000 + T)
+    dbg = _dbg_buffers(T, sh.k, sh.d, sh.f)
+    y, route = _run(x, small["wr_dev"], small["dev"], sh.k, act="mxfp4", dbg=dbg)
+    ref = oracle.route(x, small["wr"], sh.k)
+    assert_route_equal(route, ref)
+    toks = range(T) if T <= 300 else range(0, T, 5)
+    _check_mx_split(x, ref, dbg, y, small["get"], toks, sh.d, sh.f, sh.k)
+
+
 # ----------------------------------------------------------- full layer ---
 @pytest.fixture(scope="module")
 def k3layer():
