@@ -26,9 +26,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # the kernel sources whose counters profiles/traffic.json records
 TRAFFIC_SOURCES = ["mxfp4_routed_expert_softmax_amd/csrc/" + f for f in
                    ("gemv.hip", "mx.hip", "slices.hip", "route.hip", "api.hip", "device_common.h", "kernels.h",
-                    "slices.h")]
+                    "slices.h", "topk.h")]
 FFN_KERNELS = ("gateup_", "down_", "combine_", "quantize_rows", "zero_kernel", "active_list")
 MXFP4_PEAK_TFLOPS = 10100.0  # dense MXFP4 matrix peak
+EV_EVERY_DECODE = 10  # one-token steps per event-marked step (others: every step)
 
 
 def log(*a):
@@ -83,11 +84,14 @@ def main():
 
     def step(i, ev=None):
         fw.set_x(xs[i % nbatch])
-        fw.run_route()
-        if ev is not None:
+        if ev is None:
+            fw()  # k3moe_forward: the whole layer in one C call
+        else:
+            # the same work as two calls, HIP events on this stream around
+            # the expert-FFN stage (k3moe_ffn)
+            fw.run_route()
             ev[0].record(stream)
-        fw.run_ffn()
-        if ev is not None:
+            fw.run_ffn()
             ev[1].record(stream)
 
     for i in range(args.warmup):
@@ -110,14 +114,17 @@ def main():
         fw.stream = None
         torch.cuda.synchronize()
 
-    # timed region: K steps; events bracket the expert-FFN stage of each step
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # timed region: K steps; event-marked steps carry events around their
+    # expert-FFN stage.  An event record costs a few microseconds of stream
+    # time, so one-token steps (~0.1 ms) are marked one in EV_EVERY_DECODE.
+    EV_EVERY = EV_EVERY_DECODE if T == 1 else 1
+    nev = (args.steps + EV_EVERY - 1) // EV_EVERY
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     if graph is None:
         for i in range(args.steps):
-            step(i, evs[i])
+            step(i, evs[i // EV_EVERY] if i % EV_EVERY == 0 else None)
     else:
         for i in range(args.steps):
             gx.copy_(xs[i % nbatch], non_blocking=True)
@@ -141,6 +148,10 @@ def main():
                     "kernel": "expert FFN stage (every kernel k3moe_ffn launches; decode: gate/up GEMV "
                               "with SwiGLU + down GEMV with the fused combine)",
                     "bytes_per_launch": expert_bytes + act_bytes, "avg_ms": round(ffn_ms, 5)}
+        # the whole layer per step (router weights + active experts + x, y) over the timed step time
+        layer_bytes = sh.E * sh.d * 4 + expert_bytes + act_bytes
+        roofline["layer"] = {"bytes_per_step": layer_bytes,
+                             "frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if wl.act_mode == "mxfp4" and roofline is not None:
         flops = 2.0 * 3 * sh.d * sh.f * T * sh.k
         roofline["mfma_frac"] = round(flops / (roofline["avg_ms"] * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS, 4)

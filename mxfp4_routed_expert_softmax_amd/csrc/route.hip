@@ -13,6 +13,7 @@
 #include <float.h>
 #include "device_common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace k3 {
 
@@ -271,256 +272,6 @@ __device__ int block_exclusive_scan(int v, int* wave_tot, int* total)
     return excl;
 }
 
-// Top-k of one token held by one wave: lane l owns experts l, l+64, ...
-// (E <= 1024 -> at most 16 per lane).  k rounds of a wave-wide
-// (key max, index min) reduction; the winning lane retires its entry.  The
-// weight logits of the k winners are read back at the end (they equal the
-// keys unless the bias steers the selection only).
-constexpr int kMaxPerLane = 16;
-
-// (key, expert) of the better candidate: larger key, ties to the lower id;
-// be == INT_MAX marks "no candidate".
-__device__ __forceinline__ bool better(double ok, int oe, double bk, int be)
-{
-    return (oe != 0x7fffffff) && (be == 0x7fffffff || ok > bk || (ok == bk && oe < be));
-}
-
-// One exchange step of the wave argmax through a DPP lane pattern (VALU
-// latency, no LDS round trip).
-template <int CTRL>
-__device__ __forceinline__ void argmax_dpp(double& bk, int& be)
-{
-    int lo = __double2loint(bk), hi = __double2hiint(bk);
-    int olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
-    int ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
-    int oe = __builtin_amdgcn_update_dpp(be, be, CTRL, 0xF, 0xF, false);
-    double ok = __hiloint2double(ohi, olo);
-    if (better(ok, oe, bk, be)) {
-        bk = ok;
-        be = oe;
-    }
-}
-
-// Wave-wide argmax: within each row of 16 lanes by DPP (quad swaps, then
-// rotations by 4 and 8), then the four row winners compared as uniform values.
-__device__ __forceinline__ void wave_argmax(double& bk, int& be)
-{
-    argmax_dpp<0xB1>(bk, be);   // quad_perm [1,0,3,2]
-    argmax_dpp<0x4E>(bk, be);   // quad_perm [2,3,0,1]
-    argmax_dpp<0x124>(bk, be);  // row_ror:4
-    argmax_dpp<0x128>(bk, be);  // row_ror:8
-    int lo = __double2loint(bk), hi = __double2hiint(bk);
-    double rk = bk;
-    int re = be;
-    rk = __hiloint2double(__builtin_amdgcn_readlane(hi, 0), __builtin_amdgcn_readlane(lo, 0));
-    re = __builtin_amdgcn_readlane(be, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r) {
-        double ok = __hiloint2double(__builtin_amdgcn_readlane(hi, 16 * r),
-                                     __builtin_amdgcn_readlane(lo, 16 * r));
-        int oe = __builtin_amdgcn_readlane(be, 16 * r);
-        if (better(ok, oe, rk, re)) {
-            rk = ok;
-            re = oe;
-        }
-    }
-    bk = rk;
-    be = re;
-}
-
-__device__ void wave_topk(int E, int k, const double* __restrict__ lrow,
-                          const float* __restrict__ bias, int bias_select_only,
-                          int* sel_e_out, int32_t* idx_out, float* w_out)
-{
-    const int lane = threadIdx.x & 63;
-    // branch-free loads (clamped index) so all of them are in flight at once
-    double key[kMaxPerLane];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = lrow[min(e, E - 1)];
-        if (e >= E) taken |= 1u << i;
-    }
-    if (bias_select_only) {
-        float b[kMaxPerLane];
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) b[i] = bias[min(lane + 64 * i, E - 1)];
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) key[i] += (double)b[i];
-    }
-    int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-        double bk = 0.0;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
-            // ascending expert id inside the lane: strict > keeps the lower id
-            if (!((taken >> i) & 1u) && (be == 0x7fffffff || key[i] > bk)) {
-                bk = key[i];
-                be = lane + 64 * i;
-            }
-        }
-        wave_argmax(bk, be);
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        if (lane == j) my_e = be;
-    }
-    // weights: softmax over the selected weight-logits (== the full softmax
-    // restricted to the selection and renormalised)
-    double wl = (lane < k) ? lrow[my_e] : 0.0;
-    double mx = (lane < k) ? wl : -DBL_MAX;
-    for (int m = 32; m >= 1; m >>= 1) mx = fmax(mx, __shfl_xor(mx, m, 64));
-    double ex = (lane < k) ? exp(wl - mx) : 0.0;
-    double sum = ex;
-    for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
-    if (lane < k) {
-        idx_out[lane] = my_e;
-        w_out[lane] = (float)(ex / sum);
-        sel_e_out[lane] = my_e;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Block-cooperative top-k of one token (small batches, where a token's
-// selection latency is the whole cost): wave w sorts experts [64w, 64w+64)
-// with a 64-lane bitonic network in the (key descending, id ascending)
-// order, keeps its best KL (>= k) in LDS, and a tree of pairwise bitonic
-// merges reduces the lists to one.  Produces exactly the selection of
-// wave_topk (same total order), in 21 + 5 * levels exchange steps instead of
-// k serial wave-wide argmax rounds.
-__device__ __forceinline__ bool before(double ka, int ia, double kb, int ib)
-{
-    if (ia == 0x7fffffff) return false;
-    if (ib == 0x7fffffff) return true;
-    return ka > kb || (ka == kb && ia < ib);
-}
-
-template <int J>
-__device__ __forceinline__ int xchg(int v)
-{
-    if (J == 1) return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-    if (J == 2) return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-    if (J < 32) return __builtin_amdgcn_ds_swizzle(v, (J << 10) | 0x1F);
-    return __builtin_amdgcn_ds_bpermute(((int)(threadIdx.x & 63) ^ 32) << 2, v);
-}
-
-// one compare-exchange step: lanes L and L^J; the lower lane of an
-// ascending block keeps the element that comes first
-template <int J>
-__device__ __forceinline__ void bitonic_step(double& k, int& id, bool asc)
-{
-    const int lane = threadIdx.x & 63;
-    int lo = __double2loint(k), hi = __double2hiint(k);
-    int plo = xchg<J>(lo), phi = xchg<J>(hi), pid = xchg<J>(id);
-    double pk = __hiloint2double(phi, plo);
-    const bool lower = (lane & J) == 0;
-    const bool mine_first = before(k, id, pk, pid);
-    const bool keep_mine = (lower == asc) ? mine_first : !mine_first;
-    if (!keep_mine) {
-        k = pk;
-        id = pid;
-    }
-}
-
-template <int S>
-__device__ __forceinline__ void bitonic_stage(double& k, int& id)
-{
-    const bool asc = ((threadIdx.x & 63) & S) == 0 || S == 64;
-    if (S > 32) bitonic_step<32>(k, id, asc);
-    if (S > 16) bitonic_step<16>(k, id, asc);
-    if (S > 8) bitonic_step<8>(k, id, asc);
-    if (S > 4) bitonic_step<4>(k, id, asc);
-    if (S > 2) bitonic_step<2>(k, id, asc);
-    bitonic_step<1>(k, id, asc);
-}
-
-__device__ __forceinline__ void bitonic_sort64(double& k, int& id)
-{
-    bitonic_stage<2>(k, id);
-    bitonic_stage<4>(k, id);
-    bitonic_stage<8>(k, id);
-    bitonic_stage<16>(k, id);
-    bitonic_stage<32>(k, id);
-    bitonic_stage<64>(k, id);
-}
-
-constexpr int kCoopMaxT = 8;  // tokens per batch up to which the block cooperates per token
-
-// lists: LDS [16 lists][32 slots] of (key, id); KL = 16 or 32 slots used
-__device__ void block_topk_token(int E, int k, const double* __restrict__ lrow,
-                                 const float* __restrict__ bias, int bias_select_only,
-                                 double (*lk)[32], int (*li)[32],
-                                 int* sel_e_out, int32_t* idx_out, float* w_out)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int KL = k <= 16 ? 16 : 32;
-    int nl = (E + 63) / 64;  // <= 16 lists
-    if (wave < nl) {
-        const int e = 64 * wave + lane;
-        double key = 0.0;
-        int id = 0x7fffffff;
-        if (e < E) {
-            key = lrow[e];
-            if (bias_select_only) key += (double)bias[e];
-            id = e;
-        }
-        bitonic_sort64(key, id);
-        if (lane < KL) {
-            lk[wave][lane] = key;
-            li[wave][lane] = id;
-        }
-    }
-    __syncthreads();
-    while (nl > 1) {
-        const int half = (nl + 1) / 2;
-        double key = 0.0;
-        int id = 0x7fffffff;
-        if (wave < half) {
-            // lanes [0, KL): list 2w ascending; lanes [KL, 2KL): list 2w+1 reversed
-            const int a = 2 * wave, b = 2 * wave + 1;
-            if (lane < KL) {
-                key = lk[a][lane];
-                id = li[a][lane];
-            } else if (lane < 2 * KL && b < nl) {
-                key = lk[b][2 * KL - 1 - lane];
-                id = li[b][2 * KL - 1 - lane];
-            }
-        }
-        __syncthreads();
-        if (wave < half) {
-            // bitonic merge of the 2*KL lanes (ascending everywhere)
-            if (KL == 32) bitonic_step<32>(key, id, true);
-            bitonic_step<16>(key, id, true);
-            bitonic_step<8>(key, id, true);
-            bitonic_step<4>(key, id, true);
-            bitonic_step<2>(key, id, true);
-            bitonic_step<1>(key, id, true);
-            if (lane < KL) {
-                lk[wave][lane] = key;
-                li[wave][lane] = id;
-            }
-        }
-        __syncthreads();
-        nl = half;
-    }
-    if (wave == 0) {
-        // weights from the selected weight-logits, as in wave_topk
-        const int my_e = (lane < k) ? li[0][lane] : 0;
-        const double wl = (lane < k) ? lrow[my_e] : 0.0;
-        double mx = (lane < k) ? wl : -DBL_MAX;
-        for (int m = 32; m >= 1; m >>= 1) mx = fmax(mx, __shfl_xor(mx, m, 64));
-        const double ex = (lane < k) ? exp(wl - mx) : 0.0;
-        double sum = ex;
-        for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
-        if (lane < k) {
-            idx_out[lane] = my_e;
-            w_out[lane] = (float)(ex / sum);
-            sel_e_out[lane] = my_e;
-        }
-    }
-    __syncthreads();
-}
-
 // One block per 64-token chunk, 16 waves.  Writes topk_idx / topk_w, the
 // chunk's per-expert token masks and counts.  A single-chunk batch (T <= 64)
 // also finishes the grouping here: counts, offsets, perm_pair, row_of_pair.
@@ -542,11 +293,10 @@ __global__ __launch_bounds__(1024) void topk_group_kernel(
     for (int e = tid; e < E; e += blockDim.x) mask[e] = 0ull;
     __syncthreads();
     if (COOP) {
-        __shared__ double lk[16][32];
-        __shared__ int li[16][32];
+        __shared__ TopkLists lists;
         for (int tl = 0; tl < nt; ++tl) {
             int t = t0 + tl;
-            block_topk_token(E, k, logits + (size_t)t * E, bias, bias_select_only, lk, li,
+            block_topk_token(E, k, logits + (size_t)t * E, bias, bias_select_only, lists,
                              sel + tl * 32, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
         }
     } else {

@@ -196,6 +196,43 @@ def test_small_fp32_all_tokens(small, T):
     assert np.array_equal(y, y2), "not bitwise deterministic"
 
 
+def _forward_vs_split(x, wr_dev, experts, k, bias=None, bias_mode="none"):
+    """k3moe_forward against k3moe_route then k3moe_ffn on the same buffers
+    (routing outputs poisoned before each): the two must agree bit for bit."""
+    xd = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    bd = None if bias is None else torch.from_numpy(bias).to(DEV)
+    fw = k3.Forward(xd, wr_dev, experts, k, bd, bias_mode)
+    for t in fw.route.values():
+        t.fill_(-7)
+    y1 = fw().clone()
+    r1 = {n: t.clone() for n, t in fw.route.items()}
+    for t in fw.route.values():
+        t.fill_(-7)
+    fw.y.fill_(0.0)
+    fw.run_route()
+    y2 = fw.run_ffn().clone()
+    torch.cuda.synchronize()
+    for n in r1:
+        assert torch.equal(r1[n], fw.route[n]), f"routing output {n} differs"
+    assert torch.equal(y1, y2), "y differs between k3moe_forward and route + ffn"
+    return y1.cpu().numpy(), {n: t.cpu() for n, t in r1.items()}
+
+
+@pytest.mark.parametrize("bias_mode", ["none", "logits", "select_only"])
+def test_small_forward_one_token(small, bias_mode):
+    sh = small["shape"]
+    _log(f"{sh.name} one-token forward vs route + ffn, bias {bias_mode}")
+    bias = None if bias_mode == "none" else synthdata.zipf_bias(sh)
+    for rep in range(4):
+        # rep 3: x = 0, every logit 0 -- ties everywhere, the first k experts win
+        x = synthdata.tokens(sh, 1, first=4000 + rep) if rep < 3 else np.zeros((1, sh.d), np.float32)
+        y, route = _forward_vs_split(x, small["wr_dev"], small["dev"], sh.k, bias, bias_mode)
+        bm = {"none": oracle.BIAS_NONE, "logits": oracle.BIAS_LOGITS, "select_only": oracle.BIAS_SELECT_ONLY}[bias_mode]
+        ref = oracle.route(x, small["wr"], sh.k, bias, bm)
+        assert_route_equal(route, ref)
+        assert_y_close(y, oracle_y(x, ref, [0], small["get"]))
+
+
 @pytest.mark.parametrize("T", [1, 37, 600])
 def test_small_mx_split_step(small, T):
     """MXFP4 activations on layers whose d_model and d_ff are multiples of
@@ -223,6 +260,17 @@ def k3layer():
     _log("upload done")
     return dict(shape=sh, dev=dev, wr=wr, wr_dev=torch.from_numpy(wr).to(DEV),
                 get=host_expert_getter(sh), bias=synthdata.zipf_bias(sh))
+
+
+def test_k3_decode_forward_vs_split(k3layer):
+    sh = k3layer["shape"]
+    for rep in (3, 500, -1):
+        _log(f"k3 one-token forward vs route + ffn, rep {rep}")
+        # rep -1: x = 0 (all 896 logits tie: the first k experts, weights 1/k)
+        x = synthdata.tokens(sh, 1, first=rep) if rep >= 0 else np.zeros((1, sh.d), np.float32)
+        y, route = _forward_vs_split(x, k3layer["wr_dev"], k3layer["dev"], sh.k)
+        ref = oracle.route(x, k3layer["wr"], sh.k)
+        assert_route_equal(route, ref)
 
 
 def test_k3_decode_t1(k3layer):
