@@ -287,13 +287,34 @@ __global__ __launch_bounds__(1024) void topk_group_kernel(
     __shared__ int sel[kChunk * 32];
     __shared__ int offs[1025];
     __shared__ int wave_tot[17];
+    __shared__ TopkLists lists;
     const int tid = threadIdx.x, wave = tid >> 6;
     const int c = blockIdx.x, t0 = c * kChunk;
     const int nt = min(kChunk, T - t0);
+    if (COOP && T == 1) {
+        // one token: each expert's count is 0 or 1, its offset the number of
+        // chosen experts below it, a pair's row the rank of its expert
+        block_topk_token(E, k, logits, bias, bias_select_only, lists, sel, topk_idx, topk_w);
+        for (int e = tid; e <= E; e += blockDim.x) {
+            int below = 0, hit = 0;
+            for (int j = 0; j < k; ++j) {
+                below += sel[j] < e;
+                hit += sel[j] == e;
+            }
+            offsets[e] = below;
+            if (e < E) counts[e] = hit;
+        }
+        if (tid < k) {
+            int rank = 0;
+            for (int i = 0; i < k; ++i) rank += sel[i] < sel[tid];
+            perm_pair[rank] = tid;
+            row_of_pair[tid] = rank;
+        }
+        return;
+    }
     for (int e = tid; e < E; e += blockDim.x) mask[e] = 0ull;
     __syncthreads();
     if (COOP) {
-        __shared__ TopkLists lists;
         for (int tl = 0; tl < nt; ++tl) {
             int t = t0 + tl;
             block_topk_token(E, k, logits + (size_t)t * E, bias, bias_select_only, lists,
