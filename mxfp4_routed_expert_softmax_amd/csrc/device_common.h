@@ -145,6 +145,15 @@ __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint32_
         : "memory");
 }
 
+// Copy nbytes (a multiple of 1 KiB) of contiguous global memory to LDS dst:
+// the block's copies of 1 KiB go round-robin to its four waves.
+__device__ __forceinline__ void lds_copy(const uint8_t* src, uint32_t dst, int nbytes)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int j = wave; 1024 * j < nbytes; j += 4)
+        dma16(src + 1024 * j, 16u * (uint32_t)lane, dst + 1024u * (uint32_t)j);
+}
+
 // Wait until at most N vector-memory loads issued by this wave are still in
 // flight (they complete in issue order).  vmcnt sits in bits [3:0] and
 // [15:14] of the immediate; expcnt (7) and lgkmcnt (15) are left free.

@@ -452,14 +452,6 @@ __device__ __forceinline__ void b_fetch(const BSrc& b, int kc, Frag512 (&F)[2])
     }
 }
 
-// Copy nbytes (a multiple of 1 KiB) of contiguous global memory to LDS dst:
-// the block's copies of 1 KiB go round-robin to its four waves.
-__device__ __forceinline__ void lds_copy(const uint8_t* src, uint32_t dst, int nbytes)
-{
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int j = wave; 1024 * j < nbytes; j += 4)
-        dma16(src + 1024 * j, 16u * (uint32_t)lane, dst + 1024u * (uint32_t)j);
-}
 
 // Per-thread copy offsets of the A stage, fixed over the K loop: code copy q
 // of wave w moves rows 4*(4q+w) .. +3, one 16-byte piece per lane; wave 0
