@@ -46,6 +46,9 @@ def parse():
                     help="budget of host time for the oracle baseline (0 disables it)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step from a captured HIP graph instead of eager launches")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="also time steps with a read of this many MiB between them (caches cold; "
+                         "informational, reported under 'flushed')")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB three times "
                          "(reference kernel for hardware byte counters; not part of the step)")
@@ -156,6 +159,26 @@ def main():
         flops = 2.0 * 3 * sh.d * sh.f * T * sh.k
         roofline["mfma_frac"] = round(flops / (roofline["avg_ms"] * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS, 4)
 
+    flushed = None
+    if args.flush_mib > 0:
+        # each step timed alone by events on this stream, a read of a large
+        # buffer (untimed) before it, so that no weight is left in the caches
+        buf = torch.ones(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        sink = torch.zeros(1, dtype=torch.float32, device=dev)
+        nfl = min(args.steps, 100)
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nfl)]
+        for i in range(nfl):
+            sink += buf.sum()
+            fw.set_x(xs[i % nbatch])
+            fev[i][0].record(stream)
+            fw()
+            fev[i][1].record(stream)
+        torch.cuda.synchronize()
+        fms = float(np.mean([a.elapsed_time(b) for a, b in fev]))
+        flushed = {"mib": args.flush_mib, "steps": nfl, "ms_per_step": round(fms, 5),
+                   "tokens_per_s": round(T / (fms * 1e-3), 1)}
+        del buf
+
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -190,6 +213,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if flushed is not None:
+        out["flushed"] = flushed
     print(json.dumps(out), flush=True)
 
 

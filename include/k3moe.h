@@ -61,6 +61,20 @@ extern "C" {
 #define K3MOE_BIAS_LOGITS       1  /* l += b: selection and weights          */
 #define K3MOE_BIAS_SELECT_ONLY  2  /* key = l + b for selection; weights from l */
 
+/* Router score.  The workload's router scores experts by softmax over the
+ * logits (selection on the logits, weights = softmax restricted to the
+ * chosen experts and renormalised).  The pages' own router scores each
+ * expert by a sigmoid of its logit and weights the chosen experts by their
+ * bias-free sigmoid scores (fiv.co.kr deep dive, invariant #5 and the
+ * MoE-routing study-plan row); here those weights are renormalised to sum to
+ * one (the pages do not say; this is the reading taken).
+ *   SOFTMAX: key = l (+ b under SELECT_ONLY); w_j = e^{l_j} / sum_sel e^{l}
+ *   SIGMOID: s = 1/(1+e^{-l}); key = s (+ b under SELECT_ONLY);
+ *            w_j = s_j / sum_sel s
+ * (under BIAS_LOGITS, l already includes the bias). */
+#define K3MOE_SCORE_SOFTMAX  0
+#define K3MOE_SCORE_SIGMOID  1
+
 /* Activation precision inside the expert FFN. */
 #define K3MOE_ACT_FP32   0  /* x and h stay fp32; weights decoded on the fly  */
 #define K3MOE_ACT_MXFP4  1  /* x quantised per token, h per pair, to MXFP4 (OCP
@@ -118,9 +132,10 @@ int k3moe_workspace_size(const k3moe_dims *dims, int act_mode, size_t *bytes);
  *   x         fp32 [T][d_model]           (16-byte aligned)
  *   w_router  fp32 [E][d_model]           (16-byte aligned)
  *   bias      fp32 [E] or NULL (required unless bias_mode == BIAS_NONE)
+ *   bias_mode K3MOE_BIAS_*, score_fn K3MOE_SCORE_* (unknown values: ENOTSUP)
  * outputs (bit-deterministic):
  *   topk_idx    int32 [T][k]  chosen experts, descending key, ties -> lower id
- *   topk_w      fp32  [T][k]  renormalised softmax weights (sum to 1)
+ *   topk_w      fp32  [T][k]  renormalised weights (sum to 1), per score_fn
  *   counts      int32 [E]     tokens per expert
  *   offsets     int32 [E+1]   exclusive prefix sum of counts
  *   perm_pair   int32 [T*k]   row -> pair t*k+j; rows grouped by expert in
@@ -128,7 +143,7 @@ int k3moe_workspace_size(const k3moe_dims *dims, int act_mode, size_t *bytes);
  *   row_of_pair int32 [T*k]   inverse of perm_pair
  * ws: device workspace of at least k3moe_workspace_size() bytes, 256-aligned. */
 int k3moe_route(const k3moe_dims *dims, const float *x, const float *w_router,
-                const float *bias, int bias_mode,
+                const float *bias, int bias_mode, int score_fn,
                 int32_t *topk_idx, float *topk_w, int32_t *counts,
                 int32_t *offsets, int32_t *perm_pair, int32_t *row_of_pair,
                 void *ws, size_t ws_bytes, hipStream_t stream);
@@ -148,7 +163,7 @@ int k3moe_ffn(const k3moe_dims *dims, const float *x, const k3moe_experts *exper
 /* k3moe_route followed by k3moe_ffn on the same stream and workspace; every
  * routing output is still written (the caller owns those buffers). */
 int k3moe_forward(const k3moe_dims *dims, const float *x, const float *w_router,
-                  const float *bias, int bias_mode, const k3moe_experts *experts,
+                  const float *bias, int bias_mode, int score_fn, const k3moe_experts *experts,
                   int act_mode, int32_t *topk_idx, float *topk_w,
                   int32_t *counts, int32_t *offsets, int32_t *perm_pair,
                   int32_t *row_of_pair, float *y, const k3moe_debug *dbg,

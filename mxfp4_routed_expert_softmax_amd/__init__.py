@@ -20,12 +20,14 @@ LIB_PATH = os.path.join(_HERE, "libk3moe.so")
 K3MOE_OK, K3MOE_EINVAL, K3MOE_EWORKSPACE, K3MOE_ENOTSUP, K3MOE_EHIP = 0, -1, -2, -3, -4
 K3MOE_BIAS_NONE, K3MOE_BIAS_LOGITS, K3MOE_BIAS_SELECT_ONLY = 0, 1, 2
 K3MOE_ACT_FP32, K3MOE_ACT_MXFP4 = 0, 1
+K3MOE_SCORE_SOFTMAX, K3MOE_SCORE_SIGMOID = 0, 1
 
 EXPORTS = ("k3moe_workspace_size", "k3moe_route", "k3moe_ffn", "k3moe_forward",
            "k3moe_status_string", "k3moe_last_hip_error")
 
 _BIAS = {"none": K3MOE_BIAS_NONE, "logits": K3MOE_BIAS_LOGITS, "select_only": K3MOE_BIAS_SELECT_ONLY}
 _ACT = {"fp32": K3MOE_ACT_FP32, "mxfp4": K3MOE_ACT_MXFP4}
+_SCORE = {"softmax": K3MOE_SCORE_SOFTMAX, "sigmoid": K3MOE_SCORE_SIGMOID}
 
 
 class Dims(ctypes.Structure):
@@ -67,10 +69,10 @@ def _lib():
         P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         DP = ctypes.POINTER(Dims)
         L.k3moe_workspace_size.argtypes = [DP, I, ctypes.POINTER(SZ)]
-        L.k3moe_route.argtypes = [DP, P, P, P, I, P, P, P, P, P, P, P, SZ, P]
+        L.k3moe_route.argtypes = [DP, P, P, P, I, I, P, P, P, P, P, P, P, SZ, P]
         L.k3moe_ffn.argtypes = [DP, P, ctypes.POINTER(Experts), P, P, P, P, P, P, I, P,
                                 ctypes.POINTER(Debug), P, SZ, P]
-        L.k3moe_forward.argtypes = [DP, P, P, P, I, ctypes.POINTER(Experts), I, P, P, P, P, P, P, P,
+        L.k3moe_forward.argtypes = [DP, P, P, P, I, I, ctypes.POINTER(Experts), I, P, P, P, P, P, P, P,
                                     ctypes.POINTER(Debug), P, SZ, P]
         L.k3moe_status_string.argtypes = [I]
         L.k3moe_status_string.restype = ctypes.c_char_p
@@ -144,7 +146,8 @@ def alloc_route(T: int, E: int, k: int, device="cuda") -> dict:
                 perm_pair=torch.empty(T * k, **i32), row_of_pair=torch.empty(T * k, **i32))
 
 
-def k3moe_route(x, w_router, k, bias=None, bias_mode="none", out=None, ws=None, stream=None) -> dict:
+def k3moe_route(x, w_router, k, bias=None, bias_mode="none", out=None, ws=None, stream=None,
+                score_fn="softmax") -> dict:
     T, d = x.shape
     E = w_router.shape[0]
     _need(x, torch.float32, (T, d), "x")
@@ -155,7 +158,7 @@ def k3moe_route(x, w_router, k, bias=None, bias_mode="none", out=None, ws=None, 
     ws = ws if ws is not None else alloc_workspace(T, E, k, d, 32, "mxfp4", x.device)
     dims = Dims(T, E, k, d, 32)  # d_ff does not enter routing; any valid value
     rc = _lib().k3moe_route(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(bias), _BIAS[bias_mode],
-                            _ptr(out["topk_idx"]), _ptr(out["topk_w"]), _ptr(out["counts"]),
+                            _SCORE[score_fn], _ptr(out["topk_idx"]), _ptr(out["topk_w"]), _ptr(out["counts"]),
                             _ptr(out["offsets"]), _ptr(out["perm_pair"]), _ptr(out["row_of_pair"]),
                             _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "k3moe_route")
@@ -197,7 +200,7 @@ class Forward:
     activations to another tensor of the same shape."""
 
     def __init__(self, x, w_router, experts, k, bias=None, bias_mode="none", act_mode="fp32",
-                 dbg=None, stream=None):
+                 dbg=None, stream=None, score_fn="softmax"):
         T, d = x.shape
         E = w_router.shape[0]
         f = experts["gate"][0].shape[1]
@@ -215,6 +218,7 @@ class Forward:
         self._dbgp = ctypes.byref(self._dbg) if self._dbg is not None else None
         self._x = _ptr(x)
         self._bias_mode = _BIAS[bias_mode]
+        self._score = _SCORE[score_fn]
         self._act = _ACT[act_mode]
         self._wr, self._bias = _ptr(w_router), _ptr(bias)
         r = self.route
@@ -230,7 +234,7 @@ class Forward:
 
     def run_route(self):
         rc = _lib().k3moe_route(ctypes.byref(self.dims), self._x, self._wr, self._bias, self._bias_mode,
-                                *self._r, self._ws, self._wsn, _stream(self.stream))
+                                self._score, *self._r, self._ws, self._wsn, _stream(self.stream))
         _check(rc, "k3moe_route")
 
     def run_ffn(self):
@@ -241,15 +245,15 @@ class Forward:
 
     def __call__(self):
         rc = _lib().k3moe_forward(ctypes.byref(self.dims), self._x, self._wr, self._bias, self._bias_mode,
-                                  ctypes.byref(self.experts), self._act, *self._r, self._y, self._dbgp,
+                                  self._score, ctypes.byref(self.experts), self._act, *self._r, self._y, self._dbgp,
                                   self._ws, self._wsn, _stream(self.stream))
         _check(rc, "k3moe_forward")
         return self.y
 
 
 def k3moe_forward(x, w_router, experts, k, bias=None, bias_mode="none", act_mode="fp32", dbg=None,
-                  stream=None):
+                  stream=None, score_fn="softmax"):
     """Route + expert FFN + combine in one C call; returns (y, routing dict)."""
-    fw = Forward(x, w_router, experts, k, bias, bias_mode, act_mode, dbg, stream)
+    fw = Forward(x, w_router, experts, k, bias, bias_mode, act_mode, dbg, stream, score_fn)
     y = fw()
     return y, fw.route

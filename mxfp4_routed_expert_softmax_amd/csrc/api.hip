@@ -73,6 +73,11 @@ static int check_mode_act(int act_mode)
     return (act_mode == K3MOE_ACT_FP32 || act_mode == K3MOE_ACT_MXFP4) ? K3MOE_OK : K3MOE_ENOTSUP;
 }
 
+static int check_score(int score_fn)
+{
+    return (score_fn == K3MOE_SCORE_SOFTMAX || score_fn == K3MOE_SCORE_SIGMOID) ? K3MOE_OK : K3MOE_ENOTSUP;
+}
+
 static int check_mode_bias(int bias_mode, const float* bias)
 {
     if (bias_mode != K3MOE_BIAS_NONE && bias_mode != K3MOE_BIAS_LOGITS &&
@@ -138,13 +143,14 @@ static int finish_launches()
 
 // ---------------------------------------------------------------- checks ---
 static int validate_route(const k3moe_dims* dm, const float* x, const float* w_router,
-                          const float* bias, int bias_mode, int32_t* topk_idx, float* topk_w,
+                          const float* bias, int bias_mode, int score_fn, int32_t* topk_idx, float* topk_w,
                           int32_t* counts, int32_t* offsets, int32_t* perm_pair,
                           int32_t* row_of_pair, void* ws, size_t ws_bytes, int act_mode_for_ws)
 {
     int rc = check_dims(dm);
     if (rc) return rc;
     if ((rc = check_mode_bias(bias_mode, bias))) return rc;
+    if ((rc = check_score(score_fn))) return rc;
     if (dm->T == 0) return K3MOE_OK;
     if (!x || !w_router || !topk_idx || !topk_w || !counts || !offsets || !perm_pair || !row_of_pair)
         return K3MOE_EINVAL;
@@ -170,7 +176,7 @@ static int validate_ffn(const k3moe_dims* dm, const float* x, const k3moe_expert
 
 // --------------------------------------------------------------- enqueue ---
 static void enqueue_route(const k3moe_dims* dm, const float* x, const float* w_router,
-                          const float* bias, int bias_mode, int32_t* topk_idx, float* topk_w,
+                          const float* bias, int bias_mode, int score_fn, int32_t* topk_idx, float* topk_w,
                           int32_t* counts, int32_t* offsets, int32_t* perm_pair,
                           int32_t* row_of_pair, char* ws, const WsLayout& L, hipStream_t s)
 {
@@ -179,6 +185,7 @@ static void enqueue_route(const k3moe_dims* dm, const float* x, const float* w_r
                          bias_mode == K3MOE_BIAS_LOGITS, logits,
                          reinterpret_cast<double*>(ws + L.partials), s);
     launch_topk_group(dm->T, dm->E, dm->k, logits, bias, bias_mode == K3MOE_BIAS_SELECT_ONLY,
+                      score_fn == K3MOE_SCORE_SIGMOID,
                       topk_idx, topk_w, reinterpret_cast<uint64_t*>(ws + L.chunk_masks),
                       reinterpret_cast<int32_t*>(ws + L.chunk_base), counts, offsets, perm_pair,
                       row_of_pair, s);
@@ -276,17 +283,17 @@ int k3moe_workspace_size(const k3moe_dims* dims, int act_mode, size_t* bytes)
 }
 
 int k3moe_route(const k3moe_dims* dims, const float* x, const float* w_router, const float* bias,
-                int bias_mode, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                int bias_mode, int score_fn, int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
                 int32_t* perm_pair, int32_t* row_of_pair, void* ws, size_t ws_bytes,
                 hipStream_t stream)
 {
     // the routing part of the workspace is identical in both activation modes
-    int rc = validate_route(dims, x, w_router, bias, bias_mode, topk_idx, topk_w, counts, offsets,
+    int rc = validate_route(dims, x, w_router, bias, bias_mode, score_fn, topk_idx, topk_w, counts, offsets,
                             perm_pair, row_of_pair, ws, ws_bytes, -1);
     if (rc || dims->T == 0) return rc;
     if ((rc = check_device())) return rc;
     WsLayout L = ws_layout(dims->T, dims->E, dims->k, dims->d_model, dims->d_ff, K3MOE_ACT_MXFP4);
-    enqueue_route(dims, x, w_router, bias, bias_mode, topk_idx, topk_w, counts, offsets, perm_pair,
+    enqueue_route(dims, x, w_router, bias, bias_mode, score_fn, topk_idx, topk_w, counts, offsets, perm_pair,
                   row_of_pair, static_cast<char*>(ws), L, stream);
     return finish_launches();
 }
@@ -308,7 +315,7 @@ int k3moe_ffn(const k3moe_dims* dims, const float* x, const k3moe_experts* exper
 }
 
 int k3moe_forward(const k3moe_dims* dims, const float* x, const float* w_router, const float* bias,
-                  int bias_mode, const k3moe_experts* experts, int act_mode, int32_t* topk_idx,
+                  int bias_mode, int score_fn, const k3moe_experts* experts, int act_mode, int32_t* topk_idx,
                   float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm_pair,
                   int32_t* row_of_pair, float* y, const k3moe_debug* dbg, void* ws, size_t ws_bytes,
                   hipStream_t stream)
@@ -316,7 +323,7 @@ int k3moe_forward(const k3moe_dims* dims, const float* x, const float* w_router,
     int rc = check_dims(dims);
     if (rc) return rc;
     if ((rc = check_mode_act(act_mode))) return rc;
-    rc = validate_route(dims, x, w_router, bias, bias_mode, topk_idx, topk_w, counts, offsets,
+    rc = validate_route(dims, x, w_router, bias, bias_mode, score_fn, topk_idx, topk_w, counts, offsets,
                         perm_pair, row_of_pair, ws, ws_bytes, act_mode);
     if (rc) return rc;
     rc = validate_ffn(dims, x, experts, topk_idx, topk_w, counts, offsets, perm_pair, row_of_pair,
@@ -325,7 +332,7 @@ int k3moe_forward(const k3moe_dims* dims, const float* x, const float* w_router,
     if ((rc = check_device())) return rc;
     WsLayout L = ws_layout(dims->T, dims->E, dims->k, dims->d_model, dims->d_ff, act_mode);
     char* w = static_cast<char*>(ws);
-    enqueue_route(dims, x, w_router, bias, bias_mode, topk_idx, topk_w, counts, offsets, perm_pair,
+    enqueue_route(dims, x, w_router, bias, bias_mode, score_fn, topk_idx, topk_w, counts, offsets, perm_pair,
                   row_of_pair, w, L, stream);
     rc = enqueue_ffn(dims, x, experts, topk_idx, topk_w, offsets, perm_pair, row_of_pair, act_mode, y,
                      act_mode == K3MOE_ACT_MXFP4 ? dbg : nullptr, w, L, stream);

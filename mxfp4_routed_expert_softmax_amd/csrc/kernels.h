@@ -39,7 +39,7 @@ void launch_router_logits(int T, int E, int d, const float* x, const float* wr,
                           double* partials, hipStream_t s);
 // top-k + weights + per-chunk masks; for T <= 64 also the whole grouping
 void launch_topk_group(int T, int E, int k, const double* logits, const float* bias,
-                       int bias_select_only, int32_t* topk_idx, float* topk_w,
+                       int bias_select_only, int sigmoid, int32_t* topk_idx, float* topk_w,
                        uint64_t* chunk_masks, int32_t* chunk_base, int32_t* counts,
                        int32_t* offsets, int32_t* perm_pair, int32_t* row_of_pair,
                        hipStream_t s);

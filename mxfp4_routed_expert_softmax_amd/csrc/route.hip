@@ -278,7 +278,7 @@ __device__ int block_exclusive_scan(int v, int* wave_tot, int* total)
 template <bool COOP>
 __global__ __launch_bounds__(1024) void topk_group_kernel(
     int T, int E, int k, const double* __restrict__ logits, const float* __restrict__ bias,
-    int bias_select_only, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int bias_select_only, int sigmoid, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     uint64_t* __restrict__ chunk_masks, int32_t* __restrict__ chunk_cnt,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm_pair, int32_t* __restrict__ row_of_pair)
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(1024) void topk_group_kernel(
     if (COOP && T == 1) {
         // one token: each expert's count is 0 or 1, its offset the number of
         // chosen experts below it, a pair's row the rank of its expert
-        block_topk_token(E, k, logits, bias, bias_select_only, lists, sel, topk_idx, topk_w);
+        block_topk_token(E, k, logits, bias, bias_select_only, sigmoid, lists, sel, topk_idx, topk_w);
         for (int e = tid; e <= E; e += blockDim.x) {
             int below = 0, hit = 0;
             for (int j = 0; j < k; ++j) {
@@ -317,13 +317,13 @@ __global__ __launch_bounds__(1024) void topk_group_kernel(
     if (COOP) {
         for (int tl = 0; tl < nt; ++tl) {
             int t = t0 + tl;
-            block_topk_token(E, k, logits + (size_t)t * E, bias, bias_select_only, lists,
+            block_topk_token(E, k, logits + (size_t)t * E, bias, bias_select_only, sigmoid, lists,
                              sel + tl * 32, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
         }
     } else {
         for (int tl = wave; tl < nt; tl += 16) {
             int t = t0 + tl;
-            wave_topk(E, k, logits + (size_t)t * E, bias, bias_select_only, sel + tl * 32,
+            wave_topk(E, k, logits + (size_t)t * E, bias, bias_select_only, sigmoid, sel + tl * 32,
                       topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
         }
     }
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(256) void group_scatter_kernel(
 }
 
 void launch_topk_group(int T, int E, int k, const double* logits, const float* bias,
-                       int bias_select_only, int32_t* topk_idx, float* topk_w,
+                       int bias_select_only, int sigmoid, int32_t* topk_idx, float* topk_w,
                        uint64_t* chunk_masks, int32_t* chunk_base, int32_t* counts,
                        int32_t* offsets, int32_t* perm_pair, int32_t* row_of_pair,
                        hipStream_t s)
@@ -415,11 +415,11 @@ void launch_topk_group(int T, int E, int k, const double* logits, const float* b
     // chunk_base doubles as the per-chunk count array before the scan
     if (T <= kCoopMaxT)
         topk_group_kernel<true><<<dim3(nch), dim3(1024), 0, s>>>(
-            T, E, k, logits, bias, bias_select_only, topk_idx, topk_w, chunk_masks, chunk_base,
+            T, E, k, logits, bias, bias_select_only, sigmoid, topk_idx, topk_w, chunk_masks, chunk_base,
             counts, offsets, perm_pair, row_of_pair);
     else
         topk_group_kernel<false><<<dim3(nch), dim3(1024), 0, s>>>(
-            T, E, k, logits, bias, bias_select_only, topk_idx, topk_w, chunk_masks, chunk_base,
+            T, E, k, logits, bias, bias_select_only, sigmoid, topk_idx, topk_w, chunk_masks, chunk_base,
             counts, offsets, perm_pair, row_of_pair);
     if (nch > 1) {
         const int P = T * k;

@@ -74,17 +74,40 @@ __device__ __forceinline__ void bitonic_sort64(double& k, int& id)
     bitonic_stage<64>(k, id);
 }
 
+// The pages' router score: a sigmoid of the logit, in the form that never
+// overflows (1/(1+e^-l) for l >= 0, e^l/(1+e^l) below), fp64.
+__device__ __forceinline__ double sigmoid_f64(double l)
+{
+    if (l >= 0.0) return 1.0 / (1.0 + exp(-l));
+    const double el = exp(l);
+    return el / (1.0 + el);
+}
+
+// Selection key of one expert: the score (logit, or its sigmoid) plus the
+// selection-only bias.
+__device__ __forceinline__ double topk_key(double l, const float* bias, int e, int bias_select_only, int sigmoid)
+{
+    double key = sigmoid ? sigmoid_f64(l) : l;
+    if (bias_select_only) key += (double)bias[e];
+    return key;
+}
+
 // The k winners held by lanes 0..k-1 of one wave, in order (my_e, with its
 // weight-logit wl): their weights -- softmax over the selected
-// weight-logits, a fixed butterfly for the max and the sum -- and the
-// outputs (each may be null).
-__device__ __forceinline__ void topk_finish(int k, int my_e, double wl, int* sel_e_out, int32_t* idx_out,
-                                            float* w_out)
+// weight-logits, or (sigmoid) their sigmoid scores renormalised; a fixed
+// butterfly for the max and the sum -- and the outputs (each may be null).
+__device__ __forceinline__ void topk_finish(int k, int my_e, double wl, int sigmoid, int* sel_e_out,
+                                            int32_t* idx_out, float* w_out)
 {
     const int lane = threadIdx.x & 63;
-    double mx = (lane < k) ? wl : -DBL_MAX;
-    for (int m = 32; m >= 1; m >>= 1) mx = fmax(mx, __shfl_xor(mx, m, 64));
-    const double ex = (lane < k) ? exp(wl - mx) : 0.0;
+    double ex;
+    if (sigmoid) {
+        ex = (lane < k) ? sigmoid_f64(wl) : 0.0;
+    } else {
+        double mx = (lane < k) ? wl : -DBL_MAX;
+        for (int m = 32; m >= 1; m >>= 1) mx = fmax(mx, __shfl_xor(mx, m, 64));
+        ex = (lane < k) ? exp(wl - mx) : 0.0;
+    }
     double sum = ex;
     for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
     if (lane < k) {
@@ -108,7 +131,7 @@ struct TopkLists {
 // k winners in order to sel_e_out (LDS, may be null), idx_out and w_out
 // (global, may be null).  Ends with a block barrier.
 __device__ __forceinline__ void block_topk_token(int E, int k, const double* __restrict__ lrow,
-                                                 const float* __restrict__ bias, int bias_select_only,
+                                                 const float* __restrict__ bias, int bias_select_only, int sigmoid,
                                                  TopkLists& L, int* sel_e_out, int32_t* idx_out, float* w_out)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -119,8 +142,7 @@ __device__ __forceinline__ void block_topk_token(int E, int k, const double* __r
         double key = 0.0;
         int id = 0x7fffffff;
         if (e < E) {
-            key = lrow[e];
-            if (bias_select_only) key += (double)bias[e];
+            key = topk_key(lrow[e], bias, e, bias_select_only, sigmoid);
             id = e;
         }
         bitonic_sort64(key, id);
@@ -162,10 +184,11 @@ __device__ __forceinline__ void block_topk_token(int E, int k, const double* __r
         nl = half;
     }
     if (wave == 0) {
-        // without a selection-only bias the sorted key is the weight-logit itself
+        // softmax without a selection-only bias: the sorted key is the weight-logit itself
         const int my_e = (lane < k) ? L.id[bank][0][lane] : 0;
-        const double wl = (lane < k) ? (bias_select_only ? lrow[my_e] : L.key[bank][0][lane]) : 0.0;
-        topk_finish(k, my_e, wl, sel_e_out, idx_out, w_out);
+        const double wl =
+            (lane < k) ? ((bias_select_only || sigmoid) ? lrow[my_e] : L.key[bank][0][lane]) : 0.0;
+        topk_finish(k, my_e, wl, sigmoid, sel_e_out, idx_out, w_out);
     }
     __syncthreads();
 }
@@ -229,7 +252,7 @@ __device__ __forceinline__ void wave_argmax(double& bk, int& be)
 }
 
 __device__ __forceinline__ void wave_topk(int E, int k, const double* __restrict__ lrow,
-                          const float* __restrict__ bias, int bias_select_only,
+                          const float* __restrict__ bias, int bias_select_only, int sigmoid,
                           int* sel_e_out, int32_t* idx_out, float* w_out)
 {
     const int lane = threadIdx.x & 63;
@@ -241,6 +264,10 @@ __device__ __forceinline__ void wave_topk(int E, int k, const double* __restrict
         const int e = lane + 64 * i;
         key[i] = lrow[min(e, E - 1)];
         if (e >= E) taken |= 1u << i;
+    }
+    if (sigmoid) {
+#pragma unroll
+        for (int i = 0; i < kMaxPerLane; ++i) key[i] = sigmoid_f64(key[i]);
     }
     if (bias_select_only) {
         float b[kMaxPerLane];
@@ -265,7 +292,7 @@ __device__ __forceinline__ void wave_topk(int E, int k, const double* __restrict
         if ((be & 63) == lane) taken |= 1u << (be >> 6);
         if (lane == j) my_e = be;
     }
-    topk_finish(k, my_e, (lane < k) ? lrow[my_e] : 0.0, sel_e_out, idx_out, w_out);
+    topk_finish(k, my_e, (lane < k) ? lrow[my_e] : 0.0, sigmoid, sel_e_out, idx_out, w_out);
 }
 
 }  // namespace k3

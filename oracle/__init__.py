@@ -27,6 +27,7 @@ _SO = os.path.join(_HERE, "libk3oracle.so")
 _lib = None
 
 BIAS_NONE, BIAS_LOGITS, BIAS_SELECT_ONLY = 0, 1, 2
+SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
 
 
 def build(force: bool = True) -> str:
@@ -55,6 +56,8 @@ def lib():
         L.k3o_router_logits.argtypes = [I, I, I, P, P, P]
         L.k3o_select_topk.argtypes = [I, I, I, P, P]
         L.k3o_topk_weights.argtypes = [I, I, I, P, P, P]
+        L.k3o_sigmoid.argtypes = [LG, P, P]
+        L.k3o_sigmoid_weights.argtypes = [I, I, I, P, P, P]
         L.k3o_permute.argtypes, L.k3o_permute.restype = [I, I, I, P, P, P, P, P], I
         L.k3o_mx_quantize.argtypes = [LG, P, P, P]
         L.k3o_gateup.argtypes = [I, I, P, P, P, P, P, P, P, P]
@@ -141,6 +144,22 @@ def topk_weights(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return w
 
 
+def sigmoid(logits: np.ndarray) -> np.ndarray:
+    logits = _c(logits, np.float64)
+    s = np.empty_like(logits)
+    lib().k3o_sigmoid(logits.size, _p(logits), _p(s))
+    return s
+
+
+def sigmoid_weights(scores: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    scores, idx = _c(scores, np.float64), _c(idx, np.int32)
+    T, E = scores.shape
+    k = idx.shape[1]
+    w = np.empty((T, k), np.float64)
+    lib().k3o_sigmoid_weights(T, E, k, _p(scores), _p(idx), _p(w))
+    return w
+
+
 def permute(idx: np.ndarray, E: int) -> dict:
     idx = _c(idx, np.int32)
     T, k = idx.shape
@@ -154,27 +173,37 @@ def permute(idx: np.ndarray, E: int) -> dict:
     return dict(counts=counts, offsets=offsets, perm_pair=perm_pair, row_of_pair=row_of_pair)
 
 
-def route(x: np.ndarray, wr: np.ndarray, k: int, bias=None, bias_mode: int = BIAS_NONE) -> dict:
+def route(x: np.ndarray, wr: np.ndarray, k: int, bias=None, bias_mode: int = BIAS_NONE,
+          score_fn: int = SCORE_SOFTMAX) -> dict:
     """Router (O2-O5): fp64 logits, optional per-expert bias, top-k selection
-    with lower-index ties, renormalised softmax weights, expert grouping.
+    with lower-index ties, renormalised weights, expert grouping.
 
     bias_mode BIAS_LOGITS adds the bias to the logits (it changes both the
     choice and the weights); BIAS_SELECT_ONLY adds it to the selection key only
-    and weights come from the unbiased logits (fiv.co.kr deep dive, invariant
-    #5: the routing bias steers selection only)."""
+    and weights come from the unbiased scores (fiv.co.kr deep dive, invariant
+    #5: the routing bias steers selection only).
+
+    score_fn SCORE_SOFTMAX selects on the logits and weights by the softmax
+    restricted to the selection; SCORE_SIGMOID (the pages' router) scores
+    s = sigmoid(l), selects on s (+ bias under BIAS_SELECT_ONLY) and weights
+    by the chosen s renormalised to sum to one."""
     logits = router_logits(x, wr)
-    key = logits
+    b = None
     if bias is not None and bias_mode != BIAS_NONE:
         b = np.asarray(bias, np.float32).astype(np.float64)
         if bias_mode == BIAS_LOGITS:
             logits = logits + b[None, :]
-            key = logits
-        elif bias_mode == BIAS_SELECT_ONLY:
-            key = logits + b[None, :]
-        else:
+        elif bias_mode != BIAS_SELECT_ONLY:
             raise ValueError("unknown bias mode")
+    if score_fn == SCORE_SOFTMAX:
+        score = logits
+    elif score_fn == SCORE_SIGMOID:
+        score = sigmoid(logits)
+    else:
+        raise ValueError("unknown score function")
+    key = score + b[None, :] if (b is not None and bias_mode == BIAS_SELECT_ONLY) else score
     idx = select_topk(key, k)
-    w = topk_weights(logits, idx)
+    w = topk_weights(logits, idx) if score_fn == SCORE_SOFTMAX else sigmoid_weights(score, idx)
     out = dict(logits=logits, key=key, topk_idx=idx, topk_w=w)
     out.update(permute(idx, wr.shape[0]))
     return out

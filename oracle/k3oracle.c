@@ -152,6 +152,35 @@ void k3o_topk_weights(int T, int E, int k, const double *logits,
     }
 }
 
+/* Sigmoid scores (the pages' router: each expert scored by a sigmoid of its
+ * logit, [DD] invariant #5 and the MoE-routing study-plan row), in the form
+ * that never overflows: 1/(1+e^-l) for l >= 0, e^l/(1+e^l) below. */
+void k3o_sigmoid(long n, const double *l, double *s)
+{
+    for (long i = 0; i < n; ++i) {
+        const double v = l[i];
+        if (v >= 0.0) {
+            s[i] = 1.0 / (1.0 + exp(-v));
+        } else {
+            const double ev = exp(v);
+            s[i] = ev / (1.0 + ev);
+        }
+    }
+}
+
+/* Sigmoid combine weights: the chosen experts' scores, renormalised to sum
+ * to one (the pages weight by the bias-free scores; the renormalisation is
+ * the reading taken, as for softmax). */
+void k3o_sigmoid_weights(int T, int E, int k, const double *scores, const int32_t *idx, double *w)
+{
+    for (long t = 0; t < T; ++t) {
+        const double *st = scores + t * (long)E;
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j) sum += st[idx[t * k + j]];
+        for (int j = 0; j < k; ++j) w[t * k + j] = st[idx[t * k + j]] / sum;
+    }
+}
+
 /* ------------------------------------------------------------------ O5 --- */
 /* Grouping of token-expert pairs by expert (the pages' k3_moe runs "the
  * selected experts"; [DD] study plan week 4).  counts[e] = number of tokens

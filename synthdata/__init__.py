@@ -74,6 +74,9 @@ WORKLOADS = {
     "k3_batch_t64": Workload("k3_batch_t64", K3, T=64, act_mode="fp32", reps=100),
     "k3_prefill_t4096": Workload("k3_prefill_t4096", K3, T=4096, act_mode="mxfp4", reps=20),
     "k3_skew_t256": Workload("k3_skew_t256", K3, T=256, act_mode="mxfp4", zipf_bias=True, reps=100),
+    # informational: ~585 tokens per expert, past the point where the MXFP4
+    # products stop being bound by the weight stream
+    "k3_prefill_t32768": Workload("k3_prefill_t32768", K3, T=32768, act_mode="mxfp4", reps=5),
 }
 
 

@@ -72,7 +72,8 @@ def test_route_rejects_bad_arguments_without_touching_the_gpu():
     lib = k3.lib()
     dims = k3.Dims(4, 16, 2, 256, 128)
     fake = ctypes.c_void_p(0x10000)  # never dereferenced: checks fail first
-    args = [fake] * 2 + [None, 0] + [fake] * 6 + [fake, 1 << 30, None]
+    # x, w_router, bias, bias_mode, score_fn, 6 outputs, ws, ws_bytes, stream
+    args = [fake] * 2 + [None, 0, 0] + [fake] * 6 + [fake, 1 << 30, None]
     # null x
     a = list(args)
     a[0] = None
@@ -85,12 +86,18 @@ def test_route_rejects_bad_arguments_without_touching_the_gpu():
     a = list(args)
     a[3] = 9
     assert lib.k3moe_route(ctypes.byref(dims), *a) == k3.K3MOE_ENOTSUP
+    # unknown score function (refused, never defaulted)
+    a = list(args)
+    a[4] = 2
+    assert lib.k3moe_route(ctypes.byref(dims), *a) == k3.K3MOE_ENOTSUP
+    a[4] = -1
+    assert lib.k3moe_route(ctypes.byref(dims), *a) == k3.K3MOE_ENOTSUP
     # workspace too small / missing
     a = list(args)
-    a[11] = 16
+    a[12] = 16
     assert lib.k3moe_route(ctypes.byref(dims), *a) == k3.K3MOE_EWORKSPACE
     a = list(args)
-    a[10] = None
+    a[11] = None
     assert lib.k3moe_route(ctypes.byref(dims), *a) == k3.K3MOE_EWORKSPACE
     # misaligned activations
     a = list(args)
@@ -98,7 +105,7 @@ def test_route_rejects_bad_arguments_without_touching_the_gpu():
     assert lib.k3moe_route(ctypes.byref(dims), *a) == k3.K3MOE_EINVAL
     # T == 0 is a no-op that succeeds without any pointer
     z = k3.Dims(0, 16, 2, 256, 128)
-    assert lib.k3moe_route(ctypes.byref(z), *([None] * 3 + [0] + [None] * 6 + [None, 0, None])) == 0
+    assert lib.k3moe_route(ctypes.byref(z), *([None] * 3 + [0, 0] + [None] * 6 + [None, 0, None])) == 0
 
 
 def test_ffn_rejects_bad_arguments_without_touching_the_gpu():

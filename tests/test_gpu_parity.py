@@ -40,10 +40,10 @@ def tiny():
                 wr_dev=torch.from_numpy(wr).to(DEV), get=host_expert_getter(sh, host))
 
 
-def _run(x, wr_dev, experts, k, bias=None, bias_mode="none", act="fp32", dbg=None):
+def _run(x, wr_dev, experts, k, bias=None, bias_mode="none", act="fp32", dbg=None, score="softmax"):
     xd = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     bd = None if bias is None else torch.from_numpy(bias).to(DEV)
-    y, route = k3.k3moe_forward(xd, wr_dev, experts, k, bd, bias_mode, act, dbg)
+    y, route = k3.k3moe_forward(xd, wr_dev, experts, k, bd, bias_mode, act, dbg, score_fn=score)
     torch.cuda.synchronize()
     return y.cpu().numpy(), route
 
@@ -113,6 +113,23 @@ def test_tiny_bias_modes(tiny, mode):
     ref = oracle.route(x, tiny["wr"], sh.k, bias, bm)
     assert_route_equal(route, ref)
     assert_y_close(y, oracle_y(x, ref, range(40), tiny["get"]))
+
+
+_BM = {"none": 0, "logits": 1, "select_only": 2}
+
+
+@pytest.mark.parametrize("T", [5, 40])
+@pytest.mark.parametrize("mode", ["none", "logits", "select_only"])
+def test_tiny_sigmoid_router(tiny, T, mode):
+    """The pages' router: sigmoid scores, bias on the score for selection only
+    (T = 5: the block-cooperative top-k; T = 40: one wave per token)."""
+    sh = tiny["shape"]
+    bias = None if mode == "none" else synthdata.zipf_bias(sh) * np.float32(0.1)
+    x = synthdata.tokens(sh, T, first=700 + T)
+    y, route = _run(x, tiny["wr_dev"], tiny["dev"], sh.k, bias, mode, score="sigmoid")
+    ref = oracle.route(x, tiny["wr"], sh.k, bias, _BM[mode], oracle.SCORE_SIGMOID)
+    assert_route_equal(route, ref)
+    assert_y_close(y, oracle_y(x, ref, range(T), tiny["get"]))
 
 
 def test_t0_is_a_noop(tiny):
@@ -271,6 +288,19 @@ def test_k3_decode_forward_vs_split(k3layer):
         y, route = _forward_vs_split(x, k3layer["wr_dev"], k3layer["dev"], sh.k)
         ref = oracle.route(x, k3layer["wr"], sh.k)
         assert_route_equal(route, ref)
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_k3_sigmoid_router_select_only_bias(k3layer, T):
+    sh = k3layer["shape"]
+    _log(f"k3 sigmoid router, selection-only bias, T={T}")
+    bias = k3layer["bias"] * np.float32(0.05)
+    x = synthdata.tokens(sh, T, first=5000 + T)
+    y, route = _run(x, k3layer["wr_dev"], k3layer["dev"], sh.k, bias, "select_only", score="sigmoid")
+    ref = oracle.route(x, k3layer["wr"], sh.k, bias, oracle.BIAS_SELECT_ONLY, oracle.SCORE_SIGMOID)
+    assert_route_equal(route, ref)
+    toks = [0] if T == 1 else [0, 17, 63]
+    assert_y_close(y[toks], oracle_y(x, ref, toks, k3layer["get"]))
 
 
 def test_k3_decode_t1(k3layer):

@@ -138,3 +138,72 @@ def test_route_tiny_workload_end_to_end():
     r = oracle.route(x, wr, sh.k)
     _check_perm(r["topk_idx"], sh.E, r)
     assert np.allclose(r["topk_w"].sum(1), 1.0, atol=2e-15)
+
+
+# ------------------------------------------------------------ sigmoid router ---
+# The pages' router (fiv.co.kr deep dive, invariant #5 and the MoE-routing
+# study-plan row): sigmoid scores, the bias added to the score for selection
+# only, weights from the bias-free scores (renormalised here: the reading
+# taken).  Pinned against scipy's expit and brute-force sorts.
+
+def test_sigmoid_vs_scipy_expit():
+    from scipy.special import expit
+    r = np.random.default_rng(11)
+    lg = np.concatenate([r.standard_normal(2000) * 4, [0.0, 1e-300, -1e-300, 36.0, -36.0, 709.0, -745.0,
+                                                       800.0, -800.0]])[None, :]
+    s = oracle.sigmoid(lg)
+    assert np.all(np.isfinite(s)) and np.all(s >= 0) and np.all(s <= 1)
+    assert np.allclose(s, expit(lg), rtol=2e-16 * 4, atol=1e-300)
+    assert s[0, 2000] == 0.5                                   # sigma(0) exactly
+    assert np.allclose(s + oracle.sigmoid(-lg), 1.0, rtol=0, atol=2.3e-16)  # symmetry
+
+
+def test_sigmoid_selection_and_weights():
+    from scipy.special import expit
+    r = np.random.default_rng(12)
+    x = r.standard_normal((6, 64)).astype(np.float32)
+    wr = (r.standard_normal((40, 64)) / 8).astype(np.float32)
+    lg = oracle.router_logits(x, wr)
+    s = oracle.route(x, wr, 5, score_fn=oracle.SCORE_SIGMOID)
+    # sigmoid is increasing: without a bias the choice is the logits' choice
+    assert np.array_equal(s["topk_idx"], _brute_topk(lg, 5))
+    sel = np.take_along_axis(expit(lg), s["topk_idx"].astype(np.int64), axis=1)
+    assert np.allclose(s["topk_w"], sel / sel.sum(1, keepdims=True), rtol=1e-14)
+    assert np.allclose(s["topk_w"].sum(1), 1.0, rtol=0, atol=2e-15)
+    # the weights differ from the softmax ones (a dropped score function fails here)
+    m = oracle.route(x, wr, 5)
+    assert np.array_equal(m["topk_idx"], s["topk_idx"]) and not np.allclose(m["topk_w"], s["topk_w"])
+
+
+def test_sigmoid_bias_steers_selection_only():
+    from scipy.special import expit
+    r = np.random.default_rng(13)
+    x = r.standard_normal((8, 64)).astype(np.float32)
+    wr = (r.standard_normal((30, 64)) / 8).astype(np.float32)
+    b = (r.standard_normal(30) * 0.3).astype(np.float32)
+    lg = oracle.router_logits(x, wr)
+    s = oracle.route(x, wr, 4, b, oracle.BIAS_SELECT_ONLY, oracle.SCORE_SIGMOID)
+    assert np.array_equal(s["topk_idx"], _brute_topk(expit(lg) + b.astype(np.float64), 4))
+    sel = np.take_along_axis(expit(lg), s["topk_idx"].astype(np.int64), axis=1)
+    assert np.allclose(s["topk_w"], sel / sel.sum(1, keepdims=True), rtol=1e-14)
+
+
+def test_sigmoid_bias_is_added_to_the_score_not_the_logit():
+    # two experts: logits 10 and 0, bias 0.6 on the second.  On the score
+    # sigma(10) = 0.99995 < sigma(0) + 0.6 = 1.1, so the second wins; on the
+    # logit (the softmax router's selection-only bias) 10 > 0.6 keeps the first.
+    x = np.array([[1.0]], np.float32)
+    wr = np.array([[10.0], [0.0]], np.float32)
+    b = np.array([0.0, 0.6], np.float32)
+    s = oracle.route(x, wr, 1, b, oracle.BIAS_SELECT_ONLY, oracle.SCORE_SIGMOID)
+    m = oracle.route(x, wr, 1, b, oracle.BIAS_SELECT_ONLY, oracle.SCORE_SOFTMAX)
+    assert s["topk_idx"][0, 0] == 1 and m["topk_idx"][0, 0] == 0
+    assert s["topk_w"][0, 0] == 1.0
+
+
+def test_sigmoid_all_ties():
+    x = np.zeros((2, 16), np.float32)
+    wr = np.ones((12, 16), np.float32)
+    s = oracle.route(x, wr, 5, score_fn=oracle.SCORE_SIGMOID)
+    assert np.array_equal(s["topk_idx"], np.tile(np.arange(5, dtype=np.int32), (2, 1)))
+    assert np.all(s["topk_w"] == 0.2)
