@@ -1,6 +1,6 @@
 // topk.h -- top-k of one token's fp64 router logits for gfx950 wave64, by a
-// whole block (bitonic lists and merges) or by one wave (k rounds of a wave
-// argmax).  Internal to the HIP library.
+// whole block (bitonic lists, then one ranking step) or by one wave (k rounds
+// of a wave argmax).  Internal to the HIP library.
 //
 // The selection is the pages' router choice (fiv.co.kr "kimi-k3-in-c deep
 // dive", study-plan row "MoE and routing"): the k largest keys, ties to the
@@ -16,20 +16,34 @@ namespace k3 {
 constexpr int kCoopMaxT = 8;  // tokens per batch up to which a block cooperates per token
 constexpr int kTopkLists = 16;  // E <= 1024: 64 experts per list
 
-// (key, id) order: larger key first, ties to the lower id; id INT_MAX is
-// "no candidate" and sorts last.
+// (key, id) order: larger key first, ties to the lower id.  A slot without
+// a candidate holds (-inf, INT_MAX) and so sorts after every expert, whose
+// id is smaller, even one whose key is -inf.
+constexpr int kNoId = 0x7fffffff;
+
 __device__ __forceinline__ bool before(double ka, int ia, double kb, int ib)
 {
-    if (ia == 0x7fffffff) return false;
-    if (ib == 0x7fffffff) return true;
-    return ka > kb || (ka == kb && ia < ib);
+    // bitwise, not short-circuit: both tests are cheap and a branch per
+    // compare-exchange would cost more than them
+    return (ka > kb) | ((ka == kb) & (ia < ib));
 }
 
+// The value of lane L ^ J.  Inside a 16-lane row the exchange stays on the
+// vector unit (DPP; every source lane is inside the row, so no lane takes
+// the bound-control zero): J = 1, 2 are quad permutations; J = 4 is a
+// half-row mirror (L -> L ^ 7 within 8) followed by a quad reversal
+// (L -> L ^ 3); J = 8 is a rotation of the row by 8.  J = 16 and 32 cross
+// rows and go through the LDS crossbar.
 template <int J>
 __device__ __forceinline__ int xchg(int v)
 {
-    if (J == 1) return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-    if (J == 2) return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    if (J == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+    if (J == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+    if (J == 4) {
+        const int m = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true);  // row_half_mirror
+        return __builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true);          // quad_perm [3,2,1,0]
+    }
+    if (J == 8) return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);  // row_ror:8
     if (J < 32) return __builtin_amdgcn_ds_swizzle(v, (J << 10) | 0x1F);
     return __builtin_amdgcn_ds_bpermute(((int)(threadIdx.x & 63) ^ 32) << 2, v);
 }
@@ -42,14 +56,13 @@ __device__ __forceinline__ void bitonic_step(double& k, int& id, bool asc)
     const int lane = threadIdx.x & 63;
     int lo = __double2loint(k), hi = __double2hiint(k);
     int plo = xchg<J>(lo), phi = xchg<J>(hi), pid = xchg<J>(id);
-    double pk = __hiloint2double(phi, plo);
+    const double pk = __hiloint2double(phi, plo);
     const bool lower = (lane & J) == 0;
-    const bool mine_first = before(k, id, pk, pid);
-    const bool keep_mine = (lower == asc) ? mine_first : !mine_first;
-    if (!keep_mine) {
-        k = pk;
-        id = pid;
-    }
+    // the partner's element moves here when it belongs in this lane: it
+    // comes first and this is the front lane of the pair, or the reverse
+    const bool take = before(pk, pid, k, id) == (lower == asc);
+    k = take ? pk : k;
+    id = take ? pid : id;
 }
 
 template <int S>
@@ -92,24 +105,56 @@ __device__ __forceinline__ double topk_key(double l, const float* bias, int e, i
     return key;
 }
 
-// The k winners held by lanes 0..k-1 of one wave, in order (my_e, with its
-// weight-logit wl): their weights -- softmax over the selected
-// weight-logits, or (sigmoid) their sigmoid scores renormalised; a fixed
-// butterfly for the max and the sum -- and the outputs (each may be null).
-__device__ __forceinline__ void topk_finish(int k, int my_e, double wl, int sigmoid, int* sel_e_out,
-                                            int32_t* idx_out, float* w_out)
+// fp64 value of lane L ^ J (J < 32)
+template <int J>
+__device__ __forceinline__ double xchg_f64(double v)
+{
+    return __hiloint2double(xchg<J>(__double2hiint(v)), xchg<J>(__double2loint(v)));
+}
+
+// Butterflies over the lanes of each half-wave: every lane of lanes 0..31
+// ends with the max / the sum over lanes 0..31, in a fixed order.
+__device__ __forceinline__ double half_max_f64(double v)
+{
+    v = fmax(v, xchg_f64<16>(v));
+    v = fmax(v, xchg_f64<8>(v));
+    v = fmax(v, xchg_f64<4>(v));
+    v = fmax(v, xchg_f64<2>(v));
+    return fmax(v, xchg_f64<1>(v));
+}
+
+__device__ __forceinline__ double half_sum_f64(double v)
+{
+    v += xchg_f64<16>(v);
+    v += xchg_f64<8>(v);
+    v += xchg_f64<4>(v);
+    v += xchg_f64<2>(v);
+    return v + xchg_f64<1>(v);
+}
+
+// The k <= 32 winners held by lanes 0..k-1 of one (whole) wave, in order
+// (my_e, with its weight-logit wl): their weights -- softmax over the
+// selected weight-logits, or (sigmoid) their sigmoid scores renormalised --
+// and the outputs (each may be null).  max_first: lane 0's weight-logit is
+// the largest (the keys were the weight-logits themselves), so the softmax
+// maximum needs no reduction.
+__device__ __forceinline__ void topk_finish(int k, int my_e, double wl, int sigmoid, bool max_first,
+                                            int* sel_e_out, int32_t* idx_out, float* w_out)
 {
     const int lane = threadIdx.x & 63;
     double ex;
     if (sigmoid) {
         ex = (lane < k) ? sigmoid_f64(wl) : 0.0;
     } else {
-        double mx = (lane < k) ? wl : -DBL_MAX;
-        for (int m = 32; m >= 1; m >>= 1) mx = fmax(mx, __shfl_xor(mx, m, 64));
+        double mx;
+        if (max_first)
+            mx = __hiloint2double(__builtin_amdgcn_readfirstlane(__double2hiint(wl)),
+                                  __builtin_amdgcn_readfirstlane(__double2loint(wl)));
+        else
+            mx = half_max_f64((lane < k) ? wl : -DBL_MAX);
         ex = (lane < k) ? exp(wl - mx) : 0.0;
     }
-    double sum = ex;
-    for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
+    const double sum = half_sum_f64(ex);
     if (lane < k) {
         if (idx_out) idx_out[lane] = my_e;
         if (w_out) w_out[lane] = (float)(ex / sum);
@@ -117,78 +162,104 @@ __device__ __forceinline__ void topk_finish(int k, int my_e, double wl, int sigm
     }
 }
 
-// LDS of block_topk_token: two banks of up to 16 sorted lists of 32 slots
-// (the merge tree reads one bank and writes the other).
-struct TopkLists {
-    double key[2][kTopkLists][32];
-    int id[2][kTopkLists][32];
+// LDS of block_topk_token: the best KL entries of up to 16 sorted lists,
+// then the k winners in order.  An entry is one 16-byte record, read with a
+// single LDS load.
+struct __attribute__((aligned(16))) TopkEntry {
+    double key;
+    int id;
+    int pad;
 };
+struct TopkLists {
+    TopkEntry list[kTopkLists][32];
+    TopkEntry win[32];
+};
+
+// The rank of every kept entry among all kept entries: its position in its
+// own sorted list plus, for every other list, how many of that list's KL
+// entries come before it -- a binary search, since the entries that come
+// before it form a prefix of the sorted list.  Lane (group g, slot p) of
+// wave w holds entry p of list w and searches lists g, g + G, ...; the
+// groups' counts are then summed.  An entry of the overall top k is in the
+// top KL of its list, and so is every entry that beats it: its rank among
+// the kept entries is its rank among all experts.  Entries ranked below k
+// are written to L.win in rank order.
+template <int KL>
+__device__ __forceinline__ void rank_winners(int nl, int k, TopkLists& L)
+{
+    constexpr int G = 64 / KL;            // lane groups per wave
+    constexpr int MAXL = kTopkLists / G;  // lists each group searches
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int pos = lane % KL, grp = lane / KL;
+    const TopkEntry c = L.list[wave][pos];
+    int cnt[MAXL];
+    bool live[MAXL];
+    int src[MAXL];
+#pragma unroll
+    for (int j = 0; j < MAXL; ++j) {
+        const int l = grp + G * j;
+        live[j] = l < nl && l != wave;
+        src[j] = live[j] ? l : 0;  // a harmless in-range list when idle
+        cnt[j] = 0;
+    }
+#pragma unroll
+    for (int st = KL / 2; st >= 1; st >>= 1) {
+#pragma unroll
+        for (int j = 0; j < MAXL; ++j) {
+            const TopkEntry t = L.list[src[j]][cnt[j] + st - 1];
+            cnt[j] += before(t.key, t.id, c.key, c.id) ? st : 0;
+        }
+    }
+    int r = grp == 0 ? pos : 0;
+#pragma unroll
+    for (int j = 0; j < MAXL; ++j) {
+        const TopkEntry t = L.list[src[j]][cnt[j]];  // cnt <= KL - 1 here
+        const int n = cnt[j] + (before(t.key, t.id, c.key, c.id) ? 1 : 0);
+        r += live[j] ? n : 0;
+    }
+    if (G == 4) r += __builtin_amdgcn_ds_swizzle(r, (16 << 10) | 0x1F);
+    r += __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, r);
+    if (grp == 0 && r < k) L.win[r] = c;
+}
 
 // Top-k of one token by a whole block of at least E/64 waves: the experts
 // fall in lists of 64; each list is sorted by a 64-lane bitonic network
-// (DPP / swizzle exchanges) and its best KL (>= k) are kept; a tree of
-// pairwise bitonic merges reduces the lists to one.  Wave 0 then writes the
-// k winners in order to sel_e_out (LDS, may be null), idx_out and w_out
-// (global, may be null).  Ends with a block barrier.
+// (DPP / swizzle exchanges) and its best KL (>= k) are kept; one ranking
+// step (rank_winners) then orders the winners.  Wave 0 writes the k winners
+// in order to sel_e_out (LDS, may be null), idx_out and w_out (global, may
+// be null).  Ends with a block barrier.
 __device__ __forceinline__ void block_topk_token(int E, int k, const double* __restrict__ lrow,
                                                  const float* __restrict__ bias, int bias_select_only, int sigmoid,
                                                  TopkLists& L, int* sel_e_out, int32_t* idx_out, float* w_out)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int KL = k <= 16 ? 16 : 32;
-    int nl = (E + 63) / 64;  // <= nw lists (E <= 64 * waves): list w is wave w's
+    const int nl = (E + 63) / 64;  // <= waves (E <= 64 * waves): list w is wave w's
     if (wave < nl) {
         const int e = 64 * wave + lane;
-        double key = 0.0;
-        int id = 0x7fffffff;
+        double key = -__builtin_inf();
+        int id = kNoId;
         if (e < E) {
             key = topk_key(lrow[e], bias, e, bias_select_only, sigmoid);
             id = e;
         }
         bitonic_sort64(key, id);
-        if (lane < KL) {
-            L.key[0][wave][lane] = key;
-            L.id[0][wave][lane] = id;
-        }
+        if (lane < KL) L.list[wave][lane] = TopkEntry{key, id, 0};
     }
     __syncthreads();
-    int bank = 0;
-    while (nl > 1) {
-        const int half = (nl + 1) / 2;
-        for (int m = wave; m < half; m += nw) {
-            // lanes [0, KL): list 2m ascending; lanes [KL, 2KL): list 2m+1 reversed
-            const int a = 2 * m, b = 2 * m + 1;
-            double mk = 0.0;
-            int mid = 0x7fffffff;
-            if (lane < KL) {
-                mk = L.key[bank][a][lane];
-                mid = L.id[bank][a][lane];
-            } else if (lane < 2 * KL && b < nl) {
-                mk = L.key[bank][b][2 * KL - 1 - lane];
-                mid = L.id[bank][b][2 * KL - 1 - lane];
-            }
-            // bitonic merge of the 2*KL lanes (ascending everywhere)
-            if (KL == 32) bitonic_step<32>(mk, mid, true);
-            bitonic_step<16>(mk, mid, true);
-            bitonic_step<8>(mk, mid, true);
-            bitonic_step<4>(mk, mid, true);
-            bitonic_step<2>(mk, mid, true);
-            bitonic_step<1>(mk, mid, true);
-            if (lane < KL) {
-                L.key[bank ^ 1][m][lane] = mk;
-                L.id[bank ^ 1][m][lane] = mid;
-            }
-        }
-        __syncthreads();
-        bank ^= 1;
-        nl = half;
+    if (wave < nl) {
+        if (KL == 16)
+            rank_winners<16>(nl, k, L);
+        else
+            rank_winners<32>(nl, k, L);
     }
+    __syncthreads();
     if (wave == 0) {
-        // softmax without a selection-only bias: the sorted key is the weight-logit itself
-        const int my_e = (lane < k) ? L.id[bank][0][lane] : 0;
-        const double wl =
-            (lane < k) ? ((bias_select_only || sigmoid) ? lrow[my_e] : L.key[bank][0][lane]) : 0.0;
-        topk_finish(k, my_e, wl, sigmoid, sel_e_out, idx_out, w_out);
+        // softmax without a selection-only bias: the key is the weight-logit itself
+        const TopkEntry w = L.win[lane & 31];
+        const int my_e = (lane < k) ? w.id : 0;
+        const double wl = (lane < k) ? ((bias_select_only || sigmoid) ? lrow[my_e] : w.key) : 0.0;
+        topk_finish(k, my_e, wl, sigmoid, !(bias_select_only || sigmoid), sel_e_out, idx_out, w_out);
     }
     __syncthreads();
 }
@@ -292,7 +363,8 @@ __device__ __forceinline__ void wave_topk(int E, int k, const double* __restrict
         if ((be & 63) == lane) taken |= 1u << (be >> 6);
         if (lane == j) my_e = be;
     }
-    topk_finish(k, my_e, (lane < k) ? lrow[my_e] : 0.0, sigmoid, sel_e_out, idx_out, w_out);
+    topk_finish(k, my_e, (lane < k) ? lrow[my_e] : 0.0, sigmoid, !(bias_select_only || sigmoid), sel_e_out, idx_out,
+                w_out);
 }
 
 }  // namespace k3
