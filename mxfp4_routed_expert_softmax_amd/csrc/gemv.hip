@@ -486,7 +486,11 @@ __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a, const float* __
 }
 
 // ---------------------------------------------------------------------------
-static int tokens_per_pass(const FfnArgs& a) { return a.T == 1 ? 1 : 2; }
+// Tokens per pass of the grouped GEMVs: one for small batches (about two
+// tokens per active expert: the smaller register set keeps four waves per
+// SIMD and 16 weight rows in flight per wave), two once experts hold many
+// tokens (each decoded weight then serves two activation rows).
+static int tokens_per_pass(const FfnArgs& a) { return a.T <= 64 ? 1 : 2; }
 
 template <int TCH, bool PAIR>
 static void gateup_dispatch(const FfnArgs& a, float* h, hipStream_t s)

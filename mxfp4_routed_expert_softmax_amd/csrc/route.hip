@@ -272,10 +272,25 @@ __device__ int block_exclusive_scan(int v, int* wave_tot, int* total)
     return excl;
 }
 
-// One block per 64-token chunk, 16 waves.  Writes topk_idx / topk_w, the
-// chunk's per-expert token masks and counts.  A single-chunk batch (T <= 64)
-// also finishes the grouping here: counts, offsets, perm_pair, row_of_pair.
-template <bool COOP>
+// Top-k of one token per block (16 waves): the selection and the weights of
+// token blockIdx.x.
+__global__ __launch_bounds__(1024) void topk_token_kernel(int E, int k, const double* __restrict__ logits,
+                                                          const float* __restrict__ bias, int bias_select_only,
+                                                          int sigmoid, int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_w)
+{
+    __shared__ TopkLists lists;
+    const int t = blockIdx.x;
+    block_topk_token(E, k, logits + (size_t)t * E, bias, bias_select_only, sigmoid, lists, nullptr,
+                     topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+}
+
+// Grouping, one block per 64-token chunk, 16 waves.  ONE: a single token,
+// selected here too (the one-token step in one launch).  Otherwise the
+// selection is read from topk_idx; the kernel writes the chunk's per-expert
+// token masks and counts, and a single-chunk batch (T <= 64) also finishes
+// the grouping: counts, offsets, perm_pair, row_of_pair.
+template <bool ONE>
 __global__ __launch_bounds__(1024) void topk_group_kernel(
     int T, int E, int k, const double* __restrict__ logits, const float* __restrict__ bias,
     int bias_select_only, int sigmoid, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -288,10 +303,10 @@ __global__ __launch_bounds__(1024) void topk_group_kernel(
     __shared__ int offs[1025];
     __shared__ int wave_tot[17];
     __shared__ TopkLists lists;
-    const int tid = threadIdx.x, wave = tid >> 6;
+    const int tid = threadIdx.x;
     const int c = blockIdx.x, t0 = c * kChunk;
     const int nt = min(kChunk, T - t0);
-    if (COOP && T == 1) {
+    if (ONE) {
         // one token: each expert's count is 0 or 1, its offset the number of
         // chosen experts below it, a pair's row the rank of its expert
         block_topk_token(E, k, logits, bias, bias_select_only, sigmoid, lists, sel, topk_idx, topk_w);
@@ -312,21 +327,11 @@ __global__ __launch_bounds__(1024) void topk_group_kernel(
         }
         return;
     }
-    for (int e = tid; e < E; e += blockDim.x) mask[e] = 0ull;
-    __syncthreads();
-    if (COOP) {
-        for (int tl = 0; tl < nt; ++tl) {
-            int t = t0 + tl;
-            block_topk_token(E, k, logits + (size_t)t * E, bias, bias_select_only, sigmoid, lists,
-                             sel + tl * 32, topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
-        }
-    } else {
-        for (int tl = wave; tl < nt; tl += 16) {
-            int t = t0 + tl;
-            wave_topk(E, k, logits + (size_t)t * E, bias, bias_select_only, sigmoid, sel + tl * 32,
-                      topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
-        }
+    for (int i = tid; i < nt * k; i += blockDim.x) {
+        const int tl = i / k, j = i - tl * k;
+        sel[tl * 32 + j] = topk_idx[(size_t)(t0 + tl) * k + j];
     }
+    for (int e = tid; e < E; e += blockDim.x) mask[e] = 0ull;
     __syncthreads();
     for (int i = tid; i < nt * k; i += blockDim.x) {
         int tl = i / k, j = i - tl * k;
@@ -413,14 +418,17 @@ void launch_topk_group(int T, int E, int k, const double* logits, const float* b
 {
     const int nch = (T + kChunk - 1) / kChunk;
     // chunk_base doubles as the per-chunk count array before the scan
-    if (T <= kCoopMaxT)
-        topk_group_kernel<true><<<dim3(nch), dim3(1024), 0, s>>>(
-            T, E, k, logits, bias, bias_select_only, sigmoid, topk_idx, topk_w, chunk_masks, chunk_base,
-            counts, offsets, perm_pair, row_of_pair);
-    else
-        topk_group_kernel<false><<<dim3(nch), dim3(1024), 0, s>>>(
-            T, E, k, logits, bias, bias_select_only, sigmoid, topk_idx, topk_w, chunk_masks, chunk_base,
-            counts, offsets, perm_pair, row_of_pair);
+    if (T == 1) {
+        topk_group_kernel<true><<<dim3(1), dim3(1024), 0, s>>>(T, E, k, logits, bias, bias_select_only, sigmoid,
+                                                               topk_idx, topk_w, chunk_masks, chunk_base, counts,
+                                                               offsets, perm_pair, row_of_pair);
+        return;
+    }
+    topk_token_kernel<<<dim3(T), dim3(1024), 0, s>>>(E, k, logits, bias, bias_select_only, sigmoid, topk_idx,
+                                                     topk_w);
+    topk_group_kernel<false><<<dim3(nch), dim3(1024), 0, s>>>(T, E, k, logits, bias, bias_select_only, sigmoid,
+                                                              topk_idx, topk_w, chunk_masks, chunk_base, counts,
+                                                              offsets, perm_pair, row_of_pair);
     if (nch > 1) {
         const int P = T * k;
         group_scan_kernel<<<dim3(1), dim3(1024), 0, s>>>(nch, E, P, chunk_base, chunk_base,

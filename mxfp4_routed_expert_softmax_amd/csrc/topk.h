@@ -1,6 +1,6 @@
 // topk.h -- top-k of one token's fp64 router logits for gfx950 wave64, by a
-// whole block (bitonic lists, then one ranking step) or by one wave (k rounds
-// of a wave argmax).  Internal to the HIP library.
+// whole block: bitonic lists, then one ranking step.  Internal to the HIP
+// library.
 //
 // The selection is the pages' router choice (fiv.co.kr "kimi-k3-in-c deep
 // dive", study-plan row "MoE and routing"): the k largest keys, ties to the
@@ -13,7 +13,6 @@
 
 namespace k3 {
 
-constexpr int kCoopMaxT = 8;  // tokens per batch up to which a block cooperates per token
 constexpr int kTopkLists = 16;  // E <= 1024: 64 experts per list
 
 // (key, id) order: larger key first, ties to the lower id.  A slot without
@@ -262,109 +261,6 @@ __device__ __forceinline__ void block_topk_token(int E, int k, const double* __r
         topk_finish(k, my_e, wl, sigmoid, !(bias_select_only || sigmoid), sel_e_out, idx_out, w_out);
     }
     __syncthreads();
-}
-
-// Top-k of one token held by one wave (sel_e_out, idx_out, w_out may be
-// null): lane l owns experts l, l+64, ...
-// (E <= 1024 -> at most 16 per lane).  k rounds of a wave-wide
-// (key max, index min) reduction; the winning lane retires its entry.  The
-// weight logits of the k winners are read back at the end (they equal the
-// keys unless the bias steers the selection only).
-constexpr int kMaxPerLane = 16;
-
-// (key, expert) of the better candidate: larger key, ties to the lower id;
-// be == INT_MAX marks "no candidate".
-__device__ __forceinline__ bool better(double ok, int oe, double bk, int be)
-{
-    return (oe != 0x7fffffff) && (be == 0x7fffffff || ok > bk || (ok == bk && oe < be));
-}
-
-// One exchange step of the wave argmax through a DPP lane pattern (VALU
-// latency, no LDS round trip).
-template <int CTRL>
-__device__ __forceinline__ void argmax_dpp(double& bk, int& be)
-{
-    int lo = __double2loint(bk), hi = __double2hiint(bk);
-    int olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
-    int ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
-    int oe = __builtin_amdgcn_update_dpp(be, be, CTRL, 0xF, 0xF, false);
-    double ok = __hiloint2double(ohi, olo);
-    if (better(ok, oe, bk, be)) {
-        bk = ok;
-        be = oe;
-    }
-}
-
-// Wave-wide argmax: within each row of 16 lanes by DPP (quad swaps, then
-// rotations by 4 and 8), then the four row winners compared as uniform values.
-__device__ __forceinline__ void wave_argmax(double& bk, int& be)
-{
-    argmax_dpp<0xB1>(bk, be);   // quad_perm [1,0,3,2]
-    argmax_dpp<0x4E>(bk, be);   // quad_perm [2,3,0,1]
-    argmax_dpp<0x124>(bk, be);  // row_ror:4
-    argmax_dpp<0x128>(bk, be);  // row_ror:8
-    int lo = __double2loint(bk), hi = __double2hiint(bk);
-    double rk = bk;
-    int re = be;
-    rk = __hiloint2double(__builtin_amdgcn_readlane(hi, 0), __builtin_amdgcn_readlane(lo, 0));
-    re = __builtin_amdgcn_readlane(be, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r) {
-        double ok = __hiloint2double(__builtin_amdgcn_readlane(hi, 16 * r),
-                                     __builtin_amdgcn_readlane(lo, 16 * r));
-        int oe = __builtin_amdgcn_readlane(be, 16 * r);
-        if (better(ok, oe, rk, re)) {
-            rk = ok;
-            re = oe;
-        }
-    }
-    bk = rk;
-    be = re;
-}
-
-__device__ __forceinline__ void wave_topk(int E, int k, const double* __restrict__ lrow,
-                          const float* __restrict__ bias, int bias_select_only, int sigmoid,
-                          int* sel_e_out, int32_t* idx_out, float* w_out)
-{
-    const int lane = threadIdx.x & 63;
-    // branch-free loads (clamped index) so all of them are in flight at once
-    double key[kMaxPerLane];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = lrow[min(e, E - 1)];
-        if (e >= E) taken |= 1u << i;
-    }
-    if (sigmoid) {
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) key[i] = sigmoid_f64(key[i]);
-    }
-    if (bias_select_only) {
-        float b[kMaxPerLane];
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) b[i] = bias[min(lane + 64 * i, E - 1)];
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) key[i] += (double)b[i];
-    }
-    int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-        double bk = 0.0;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
-            // ascending expert id inside the lane: strict > keeps the lower id
-            if (!((taken >> i) & 1u) && (be == 0x7fffffff || key[i] > bk)) {
-                bk = key[i];
-                be = lane + 64 * i;
-            }
-        }
-        wave_argmax(bk, be);
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        if (lane == j) my_e = be;
-    }
-    topk_finish(k, my_e, (lane < k) ? lrow[my_e] : 0.0, sigmoid, !(bias_select_only || sigmoid), sel_e_out, idx_out,
-                w_out);
 }
 
 }  // namespace k3
