@@ -29,6 +29,14 @@ WsLayout ws_layout(int T, int E, int k, int d, int f, int act_mode)
     L.chunk_masks = take(nch * E * sizeof(uint64_t));
     L.chunk_base = take(nch * E * sizeof(int32_t));
     L.active = take(((size_t)E + 1) * sizeof(int32_t));
+    {
+        const bool i8 = use_router_i8(T, E, k, d);
+        L.rsl_x = take(i8 ? (size_t)6 * T * d : 0);
+        L.rsl_w = take(i8 ? (size_t)6 * E * d : 0);
+        L.rsl_xe = take(i8 ? (size_t)T * sizeof(int) : 0);
+        L.rsl_we = take(i8 ? (size_t)E * sizeof(int) : 0);
+        L.rsl_wc = take(i8 ? (size_t)E * sizeof(double) : 0);
+    }
     L.route_total = off;
     if (act_mode == K3MOE_ACT_FP32) {
         L.h = take(P * f * sizeof(float));
@@ -181,14 +189,25 @@ static void enqueue_route(const k3moe_dims* dm, const float* x, const float* w_r
                           int32_t* row_of_pair, char* ws, const WsLayout& L, hipStream_t s)
 {
     double* logits = reinterpret_cast<double*>(ws + L.logits);
-    launch_router_logits(dm->T, dm->E, dm->d_model, x, w_router, bias,
-                         bias_mode == K3MOE_BIAS_LOGITS, logits,
-                         reinterpret_cast<double*>(ws + L.partials), s);
+    const int bias_in_logits = bias_mode == K3MOE_BIAS_LOGITS;
+    TopkCert cert{nullptr, nullptr, x, w_router, dm->d_model, bias_in_logits};
+    if (use_router_i8(dm->T, dm->E, dm->k, dm->d_model) && aligned(x, 16) && aligned(w_router, 16)) {
+        int* xe = reinterpret_cast<int*>(ws + L.rsl_xe);
+        double* wc = reinterpret_cast<double*>(ws + L.rsl_wc);
+        launch_router_i8(dm->T, dm->E, dm->d_model, x, w_router, bias, bias_in_logits,
+                         reinterpret_cast<int8_t*>(ws + L.rsl_x), reinterpret_cast<int8_t*>(ws + L.rsl_w), xe,
+                         reinterpret_cast<int*>(ws + L.rsl_we), wc, logits, s);
+        cert.xe = xe;
+        cert.wc = wc;
+    } else {
+        launch_router_logits(dm->T, dm->E, dm->d_model, x, w_router, bias, bias_in_logits, logits,
+                             reinterpret_cast<double*>(ws + L.partials), s);
+    }
     launch_topk_group(dm->T, dm->E, dm->k, logits, bias, bias_mode == K3MOE_BIAS_SELECT_ONLY,
                       score_fn == K3MOE_SCORE_SIGMOID,
                       topk_idx, topk_w, reinterpret_cast<uint64_t*>(ws + L.chunk_masks),
                       reinterpret_cast<int32_t*>(ws + L.chunk_base), counts, offsets, perm_pair,
-                      row_of_pair, s);
+                      row_of_pair, cert, s);
 }
 
 static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts* ex,

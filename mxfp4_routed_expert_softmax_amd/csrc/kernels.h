@@ -17,6 +17,11 @@ struct WsLayout {
     size_t chunk_masks;  // uint64 [nch][E]          which chunk tokens chose e
     size_t chunk_base;   // int32  [nch][E]          rows of e before chunk c
     size_t active;       // int32  [E + 1]           active experts, count last
+    size_t rsl_x;        // int8   [6][T][d]         int8 router: slices of x
+    size_t rsl_w;        // int8   [6][E][d]         int8 router: slices of W_r
+    size_t rsl_xe;       // int32  [T]               int8 router: row exponents of x
+    size_t rsl_we;       // int32  [E]               int8 router: row exponents of W_r
+    size_t rsl_wc;       // double [E]               int8 router: bound factors
     size_t route_total;  // bytes the routing calls need (a prefix of the rest)
     size_t h;            // fp32   [T*k][f]          fp32 mode: SwiGLU output
     size_t o;            // fp32   [T*k][d]          fp32 mode: per-pair down
@@ -37,12 +42,29 @@ int router_splits(int T, int E, int d);
 void launch_router_logits(int T, int E, int d, const float* x, const float* wr,
                           const float* bias, int bias_in_logits, double* logits,
                           double* partials, hipStream_t s);
+// Large batches: logits from int8 slices of x and W_r (exact int32 products,
+// fp64 combination) with a rigorous per-token bound, for the certified
+// top-k.  The workspace regions rsl_* above.
+constexpr int kRouterI8MinT = 1024;
+bool use_router_i8(int T, int E, int k, int d);
+void launch_router_i8(int T, int E, int d, const float* x, const float* wr, const float* bias, int bias_in_logits,
+                      int8_t* xs, int8_t* wsl, int* xe, int* we, double* wc, double* logits, hipStream_t s);
+// What the top-k needs to certify int8 logits (xe null: exact fp64 logits)
+struct TopkCert {
+    const int* xe;
+    const double* wc;
+    const float* x;
+    const float* wr;
+    int d;
+    int bias_in_logits;
+};
 // top-k + weights + per-chunk masks; for T <= 64 also the whole grouping
-void launch_topk_group(int T, int E, int k, const double* logits, const float* bias,
+// (logits: rewritten for a token whose certification fails)
+void launch_topk_group(int T, int E, int k, double* logits, const float* bias,
                        int bias_select_only, int sigmoid, int32_t* topk_idx, float* topk_w,
                        uint64_t* chunk_masks, int32_t* chunk_base, int32_t* counts,
                        int32_t* offsets, int32_t* perm_pair, int32_t* row_of_pair,
-                       hipStream_t s);
+                       const TopkCert& cert, hipStream_t s);
 void launch_active_list(int E, const int32_t* offsets, int32_t* active, hipStream_t s);
 
 // ---- fp32-activation expert path (GEMV family) ----------------------------

@@ -208,6 +208,209 @@ __global__ __launch_bounds__(256) void router_bias_kernel(long n, int E, const f
     if (i < n) logits[i] += (double)bias[i % E];
 }
 
+// ---------------------------------------------------------------------------
+// Router logits for large batches on the int8 matrix cores, certified.
+//
+// Error-free splitting of the operands (the scheme of Ozaki, Ogita, Oishi and
+// Rump for matrix products, in its integer form): every row v of x and of
+// W_r is scaled by 2^-a, a its exponent (max |v| < 2^a), and cut by
+// truncation into kSl signed 7-bit slices, v = 2^a (sum_p V_p 2^-7(p+1) +
+// r 2^-7kSl) with |r| < 1 -- each step exact in fp32.  The logit x.w is then
+// taken as the slice pairs with p + q <= kSl - 1 (21 of the 36), each an int8
+// dot product summed exactly in int32 on the matrix cores, combined in fp64.
+// Against the exact x.w this is off by less than
+//   2^(a_x - 7 kSl) (kSl d 2^a_w + |w|_1)
+// (truncation of x after kSl slices, and for each slice p of x the
+// truncation of w after kSl - p slices), and the fp64 sums -- ours and the
+// oracle's sequential one -- add at most 2 (d + 8) 2^-53 2^a_x |w|_1 more.
+// wc[e] holds that bound's factor of 2^a_x for row e; the top-k of each token
+// then checks that every gap among its best k + 1 keys exceeds twice the
+// token's bound, and recomputes the token's logits exactly in fp64 where one
+// does not (ties, near-ties, an all-zero token), so the selection is the
+// exact-arithmetic one in every case.
+constexpr int kSl = 6;           // slices per operand
+constexpr int kZeroRow = -100000;  // exponent marker of an all-zero row
+
+// One row per block (x rows first, then W_r rows): its exponent, its slices
+// ([kSl][rows][d] int8) and, for W_r rows, the bound factor.
+__global__ __launch_bounds__(256) void router_slice_kernel(int T, int E, int d, const float* __restrict__ x,
+                                                           const float* __restrict__ wr, int8_t* __restrict__ xs,
+                                                           int8_t* __restrict__ wsl, int* __restrict__ xe,
+                                                           int* __restrict__ we, double* __restrict__ wc)
+{
+    __shared__ float redm[4];
+    __shared__ double redn[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool isx = (int)blockIdx.x < T;
+    const int r = isx ? (int)blockIdx.x : (int)blockIdx.x - T, rows = isx ? T : E;
+    const float* v = (isx ? x : wr) + (size_t)r * d;
+    int8_t* out = (isx ? xs : wsl) + (size_t)r * d;
+    const size_t pstride = (size_t)rows * d;
+    float m = 0.f;
+    double n1 = 0.0;
+    for (int i = 4 * tid; i < d; i += 1024) {
+        const float4 f = *reinterpret_cast<const float4*>(v + i);
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+        n1 += ((double)fabsf(f.x) + (double)fabsf(f.y)) + ((double)fabsf(f.z) + (double)fabsf(f.w));
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+        m = fmaxf(m, __shfl_xor(m, o, 64));
+        n1 += __shfl_xor(n1, o, 64);
+    }
+    if (lane == 0) {
+        redm[wave] = m;
+        redn[wave] = n1;
+    }
+    __syncthreads();
+    m = fmaxf(fmaxf(redm[0], redm[1]), fmaxf(redm[2], redm[3]));
+    n1 = (redn[0] + redn[1]) + (redn[2] + redn[3]);
+    int a = kZeroRow;
+    if (m > 0.f) (void)frexpf(m, &a);  // m < 2^a
+    const int sh = m > 0.f ? -a : 0;
+    for (int i = 4 * tid; i < d; i += 1024) {
+        const float4 f = *reinterpret_cast<const float4*>(v + i);
+        float u[4] = {ldexpf(f.x, sh), ldexpf(f.y, sh), ldexpf(f.z, sh), ldexpf(f.w, sh)};
+#pragma unroll
+        for (int p = 0; p < kSl; ++p) {
+            uint32_t packed = 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float t = u[j] * 128.0f;
+                const float q = truncf(t);  // |q| <= 127
+                u[j] = t - q;               // exact: the fraction of t
+                packed |= ((uint32_t)(int)q & 0xffu) << (8 * j);
+            }
+            *reinterpret_cast<uint32_t*>(out + (size_t)p * pstride + i) = packed;
+        }
+    }
+    if (tid == 0) {
+        if (isx) {
+            xe[r] = a;
+        } else {
+            we[r] = a;
+            // |w|_1 rounded up (the fp64 sum of d exact terms is within d 2^-53 of it)
+            const double w1 = n1 * (1.0 + 0x1p-30);
+            const double c = ldexp((double)kSl * d * ldexp(1.0, m > 0.f ? a : -1000) + w1, -7 * kSl) +
+                             2.0 * (d + 8) * 0x1p-53 * w1;
+            wc[r] = c * (1.0 + 0x1p-20);
+        }
+    }
+}
+
+// Logits of a 64-token x 64-expert tile: four waves, each a 32 x 32 corner as
+// 2 x 2 tiles of V_MFMA_I32_16X16X64_I8, one int32 accumulator set per slice
+// level p + q.  Per 64-wide K step the kSl slices of both operands go through
+// LDS (rows padded to 80 bytes: the 16 rows of a fragment read fall on
+// distinct banks), the next step's slices already in flight in registers.
+// Lane l supplies A[l%16][16(l/16) .. +15] and B[same][l%16]; it receives
+// D[4(l/16) + v][l%16].
+constexpr int kI8Row = 80;
+
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void router_i8_kernel(
+    int T, int E, int d, const int8_t* __restrict__ xs, const int8_t* __restrict__ wsl, const int* __restrict__ xe,
+    const int* __restrict__ we, const float* __restrict__ bias, int bias_in_logits, double* __restrict__ logits)
+{
+    __shared__ __attribute__((aligned(16))) int8_t As[kSl][64 * kI8Row];
+    __shared__ __attribute__((aligned(16))) int8_t Bs[kSl][64 * kI8Row];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1, li = lane & 15, g = lane >> 4;
+    const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
+    // staging: thread -> (row, 16-byte piece c) of every slice; rows past the
+    // end repeat the last row (their results are discarded)
+    const int srow = tid >> 2, sc = tid & 3;
+    const size_t xoff = (size_t)min(t0 + srow, T - 1) * d + 16 * sc;
+    const size_t woff = (size_t)min(e0 + srow, E - 1) * d + 16 * sc;
+    const size_t xps = (size_t)T * d, wps = (size_t)E * d;
+    const int8_t* xsrc = xs + xoff;
+    const int8_t* wsrc = wsl + woff;
+    i32x4v acc[kSl][2][2];
+#pragma unroll
+    for (int l = 0; l < kSl; ++l)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) acc[l][mi][ni] = (i32x4v){0, 0, 0, 0};
+    i32x4v ra[kSl], rb[kSl];
+#pragma unroll
+    for (int p = 0; p < kSl; ++p) {
+        ra[p] = *reinterpret_cast<const i32x4v*>(xsrc + p * xps);
+        rb[p] = *reinterpret_cast<const i32x4v*>(wsrc + p * wps);
+    }
+    for (int k0 = 0; k0 < d; k0 += 64) {
+        __syncthreads();  // every wave is done with the previous step's LDS
+#pragma unroll
+        for (int p = 0; p < kSl; ++p) {
+            *reinterpret_cast<i32x4v*>(&As[p][srow * kI8Row + 16 * sc]) = ra[p];
+            *reinterpret_cast<i32x4v*>(&Bs[p][srow * kI8Row + 16 * sc]) = rb[p];
+        }
+        __syncthreads();
+        {
+            // the next step's slices, in flight during this step's matrix work
+            // (the last step fetches its own chunk again: branch-free)
+            const int kn = min(k0 + 64, d - 64);
+#pragma unroll
+            for (int p = 0; p < kSl; ++p) {
+                ra[p] = *reinterpret_cast<const i32x4v*>(xsrc + p * xps + kn);
+                rb[p] = *reinterpret_cast<const i32x4v*>(wsrc + p * wps + kn);
+            }
+        }
+        i32x4v bf[kSl][2];
+#pragma unroll
+        for (int q = 0; q < kSl; ++q)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                bf[q][ni] = *reinterpret_cast<const i32x4v*>(&Bs[q][(32 * wn + 16 * ni + li) * kI8Row + 16 * g]);
+#pragma unroll
+        for (int p = 0; p < kSl; ++p) {
+            i32x4v af[2];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+                af[mi] = *reinterpret_cast<const i32x4v*>(&As[p][(32 * wm + 16 * mi + li) * kI8Row + 16 * g]);
+#pragma unroll
+            for (int q = 0; q + p < kSl; ++q)
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni)
+                        acc[p + q][mi][ni] =
+                            __builtin_amdgcn_mfma_i32_16x16x64_i8(af[mi], bf[q][ni], acc[p + q][mi][ni], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = t0 + 32 * wm + 16 * mi + 4 * g + v;
+                const int e = e0 + 32 * wn + 16 * ni + li;
+                if (t < T && e < E) {
+                    double sum = 0.0;  // level l = p + q carries 2^-7(l+2); every term exact
+#pragma unroll
+                    for (int l = kSl - 1; l >= 0; --l) sum += ldexp((double)acc[l][mi][ni][v], -7 * (l + 2));
+                    const int ax = xe[t], aw = we[e];
+                    double lg = (ax == kZeroRow || aw == kZeroRow) ? 0.0 : ldexp(sum, ax + aw);
+                    if (bias_in_logits) lg += (double)bias[e];
+                    logits[(size_t)t * E + e] = lg;
+                }
+            }
+}
+
+bool use_router_i8(int T, int E, int k, int d)
+{
+    return T >= kRouterI8MinT && k < 32 && k < E && d % 64 == 0 && d <= 16384 && E <= 1024;
+}
+
+void launch_router_i8(int T, int E, int d, const float* x, const float* wr, const float* bias, int bias_in_logits,
+                      int8_t* xs, int8_t* wsl, int* xe, int* we, double* wc, double* logits, hipStream_t s)
+{
+    router_slice_kernel<<<dim3(T + E), dim3(256), 0, s>>>(T, E, d, x, wr, xs, wsl, xe, we, wc);
+    router_i8_kernel<<<dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s>>>(T, E, d, xs, wsl, xe, we, bias,
+                                                                           bias_in_logits, logits);
+}
+
 int router_splits(int T, int E, int d)
 {
     if (T <= kGemvTok) return 1;
@@ -272,17 +475,55 @@ __device__ int block_exclusive_scan(int v, int* wave_tot, int* total)
     return excl;
 }
 
+// Logits of one token, exactly as router_rows forms them (fp64 sums of the
+// exact fp32 x fp32 products), one wave per expert row: the fallback of the
+// certified selection.
+__device__ __forceinline__ void exact_logits_row(int E, int d, const float* __restrict__ xrow,
+                                                 const float* __restrict__ wr, const float* __restrict__ bias,
+                                                 int bias_in_logits, double* __restrict__ lrow)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    for (int e = wave; e < E; e += nw) {
+        const float* w = wr + (size_t)e * d;
+        double acc = 0.0;
+        for (int i = lane; i < d; i += 64) acc = fma((double)xrow[i], (double)w[i], acc);
+        for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+        if (lane == 0) lrow[e] = bias_in_logits ? acc + (double)bias[e] : acc;
+    }
+}
+
 // Top-k of one token per block (16 waves): the selection and the weights of
-// token blockIdx.x.
-__global__ __launch_bounds__(1024) void topk_token_kernel(int E, int k, const double* __restrict__ logits,
+// token blockIdx.x.  With xe (logits from the int8 slices): the selection is
+// certified against the token's bound 2^a_x max_e wc[e], and a token that
+// fails gets its logits recomputed exactly (written back) and selected again.
+__global__ __launch_bounds__(1024) void topk_token_kernel(int E, int k, double* __restrict__ logits,
                                                           const float* __restrict__ bias, int bias_select_only,
                                                           int sigmoid, int32_t* __restrict__ topk_idx,
-                                                          float* __restrict__ topk_w)
+                                                          float* __restrict__ topk_w, const int* __restrict__ xe,
+                                                          const double* __restrict__ wc, const float* __restrict__ x,
+                                                          const float* __restrict__ wr, int d, int bias_in_logits)
 {
     __shared__ TopkLists lists;
-    const int t = blockIdx.x;
-    block_topk_token(E, k, logits + (size_t)t * E, bias, bias_select_only, sigmoid, lists, nullptr,
-                     topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+    __shared__ double redc[16];
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    double* lrow = logits + (size_t)t * E;
+    int32_t* idx = topk_idx + (size_t)t * k;
+    float* w = topk_w + (size_t)t * k;
+    if (xe) {
+        double c = 0.0;
+        for (int e = tid; e < E; e += blockDim.x) c = fmax(c, wc[e]);
+        for (int o = 32; o >= 1; o >>= 1) c = fmax(c, __shfl_xor(c, o, 64));
+        if (lane == 0) redc[wave] = c;
+        __syncthreads();
+        double cmax = 0.0;
+        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) cmax = fmax(cmax, redc[i]);
+        const int ax = xe[t];
+        const double bound = ax == kZeroRow ? 0.0 : ldexp(cmax, ax);
+        if (block_topk_token(E, k, lrow, bias, bias_select_only, sigmoid, lists, nullptr, idx, w, bound)) return;
+        exact_logits_row(E, d, x + (size_t)t * d, wr, bias, bias_in_logits, lrow);
+        __syncthreads();
+    }
+    block_topk_token(E, k, lrow, bias, bias_select_only, sigmoid, lists, nullptr, idx, w);
 }
 
 // Grouping, one block per 64-token chunk, 16 waves.  ONE: a single token,
@@ -410,11 +651,11 @@ __global__ __launch_bounds__(256) void group_scatter_kernel(
     row_of_pair[p] = row;
 }
 
-void launch_topk_group(int T, int E, int k, const double* logits, const float* bias,
+void launch_topk_group(int T, int E, int k, double* logits, const float* bias,
                        int bias_select_only, int sigmoid, int32_t* topk_idx, float* topk_w,
                        uint64_t* chunk_masks, int32_t* chunk_base, int32_t* counts,
                        int32_t* offsets, int32_t* perm_pair, int32_t* row_of_pair,
-                       hipStream_t s)
+                       const TopkCert& cert, hipStream_t s)
 {
     const int nch = (T + kChunk - 1) / kChunk;
     // chunk_base doubles as the per-chunk count array before the scan
@@ -425,7 +666,8 @@ void launch_topk_group(int T, int E, int k, const double* logits, const float* b
         return;
     }
     topk_token_kernel<<<dim3(T), dim3(1024), 0, s>>>(E, k, logits, bias, bias_select_only, sigmoid, topk_idx,
-                                                     topk_w);
+                                                     topk_w, cert.xe, cert.wc, cert.x, cert.wr, cert.d,
+                                                     cert.bias_in_logits);
     topk_group_kernel<false><<<dim3(nch), dim3(1024), 0, s>>>(T, E, k, logits, bias, bias_select_only, sigmoid,
                                                               topk_idx, topk_w, chunk_masks, chunk_base, counts,
                                                               offsets, perm_pair, row_of_pair);

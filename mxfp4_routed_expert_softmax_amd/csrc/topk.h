@@ -172,6 +172,7 @@ struct __attribute__((aligned(16))) TopkEntry {
 struct TopkLists {
     TopkEntry list[kTopkLists][32];
     TopkEntry win[32];
+    int ok;
 };
 
 // The rank of every kept entry among all kept entries: its position in its
@@ -223,16 +224,26 @@ __device__ __forceinline__ void rank_winners(int nl, int k, TopkLists& L)
 
 // Top-k of one token by a whole block of at least E/64 waves: the experts
 // fall in lists of 64; each list is sorted by a 64-lane bitonic network
-// (DPP / swizzle exchanges) and its best KL (>= k) are kept; one ranking
-// step (rank_winners) then orders the winners.  Wave 0 writes the k winners
-// in order to sel_e_out (LDS, may be null), idx_out and w_out (global, may
-// be null).  Ends with a block barrier.
-__device__ __forceinline__ void block_topk_token(int E, int k, const double* __restrict__ lrow,
+// (DPP / swizzle exchanges) and its best KL (>= the winners needed) are
+// kept; one ranking step (rank_winners) then orders the winners.  Wave 0
+// writes the k winners in order to sel_e_out (LDS, may be null), idx_out and
+// w_out (global, may be null).  Ends with a block barrier.
+//
+// With a bound (>= 0, k < E): the keys are approximations within bound of
+// the exact ones, and the selection is kept only if every gap among the best
+// k + 1 keys exceeds twice the bound (and a relative 2^-40 for the fp64
+// rounding of the keys themselves) -- then the exact keys have the same
+// winners in the same order.  Otherwise nothing is written and false comes
+// back (block-uniform).
+__device__ __forceinline__ bool block_topk_token(int E, int k, const double* __restrict__ lrow,
                                                  const float* __restrict__ bias, int bias_select_only, int sigmoid,
-                                                 TopkLists& L, int* sel_e_out, int32_t* idx_out, float* w_out)
+                                                 TopkLists& L, int* sel_e_out, int32_t* idx_out, float* w_out,
+                                                 double bound = -1.0)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int KL = k <= 16 ? 16 : 32;
+    const bool cert = bound >= 0.0;
+    const int kk = cert ? k + 1 : k;
+    const int KL = kk <= 16 ? 16 : 32;
     const int nl = (E + 63) / 64;  // <= waves (E <= 64 * waves): list w is wave w's
     if (wave < nl) {
         const int e = 64 * wave + lane;
@@ -248,11 +259,23 @@ __device__ __forceinline__ void block_topk_token(int E, int k, const double* __r
     __syncthreads();
     if (wave < nl) {
         if (KL == 16)
-            rank_winners<16>(nl, k, L);
+            rank_winners<16>(nl, kk, L);
         else
-            rank_winners<32>(nl, k, L);
+            rank_winners<32>(nl, kk, L);
     }
     __syncthreads();
+    if (cert) {
+        if (threadIdx.x == 0) {
+            bool ok = true;
+            for (int j = 0; j + 1 < kk; ++j) {
+                const double a = L.win[j].key, b = L.win[j + 1].key;
+                ok = ok && (a - b > 2.0 * bound + 0x1p-40 * (fabs(a) + fabs(b)));
+            }
+            L.ok = ok ? 1 : 0;
+        }
+        __syncthreads();
+        if (!L.ok) return false;
+    }
     if (wave == 0) {
         // softmax without a selection-only bias: the key is the weight-logit itself
         const TopkEntry w = L.win[lane & 31];
@@ -261,6 +284,7 @@ __device__ __forceinline__ void block_topk_token(int E, int k, const double* __r
         topk_finish(k, my_e, wl, sigmoid, !(bias_select_only || sigmoid), sel_e_out, idx_out, w_out);
     }
     __syncthreads();
+    return true;
 }
 
 }  // namespace k3

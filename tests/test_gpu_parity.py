@@ -48,7 +48,7 @@ def _run(x, wr_dev, experts, k, bias=None, bias_mode="none", act="fp32", dbg=Non
     return y.cpu().numpy(), route
 
 
-@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 130])
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 130, 1100])
 def test_tiny_fp32_all_tokens(tiny, T):
     sh = tiny["shape"]
     _log(f"tiny fp32 T={T}")
@@ -103,32 +103,56 @@ def test_tiny_k_extremes(tiny, k):
     assert_y_close(y, oracle_y(x, ref, range(5), tiny["get"]))
 
 
+@pytest.mark.parametrize("T", [40, 1100])
 @pytest.mark.parametrize("mode", ["logits", "select_only"])
-def test_tiny_bias_modes(tiny, mode):
+def test_tiny_bias_modes(tiny, mode, T):
     sh = tiny["shape"]
     bias = synthdata.zipf_bias(sh)
-    x = synthdata.tokens(sh, 40, first=300)
+    x = synthdata.tokens(sh, T, first=300)
     y, route = _run(x, tiny["wr_dev"], tiny["dev"], sh.k, bias, mode)
     bm = oracle.BIAS_LOGITS if mode == "logits" else oracle.BIAS_SELECT_ONLY
     ref = oracle.route(x, tiny["wr"], sh.k, bias, bm)
     assert_route_equal(route, ref)
-    assert_y_close(y, oracle_y(x, ref, range(40), tiny["get"]))
+    assert_y_close(y, oracle_y(x, ref, range(T), tiny["get"]))
 
 
 _BM = {"none": 0, "logits": 1, "select_only": 2}
 
 
-@pytest.mark.parametrize("T", [5, 40])
+@pytest.mark.parametrize("T", [5, 40, 1100])
 @pytest.mark.parametrize("mode", ["none", "logits", "select_only"])
 def test_tiny_sigmoid_router(tiny, T, mode):
     """The pages' router: sigmoid scores, bias on the score for selection only
-    (T = 5: the block-cooperative top-k; T = 40: one wave per token)."""
+    (T = 1100: logits from the int8 slices, certified selection)."""
     sh = tiny["shape"]
     bias = None if mode == "none" else synthdata.zipf_bias(sh) * np.float32(0.1)
     x = synthdata.tokens(sh, T, first=700 + T)
     y, route = _run(x, tiny["wr_dev"], tiny["dev"], sh.k, bias, mode, score="sigmoid")
     ref = oracle.route(x, tiny["wr"], sh.k, bias, _BM[mode], oracle.SCORE_SIGMOID)
     assert_route_equal(route, ref)
+    assert_y_close(y, oracle_y(x, ref, range(T), tiny["get"]))
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+def test_tiny_int8_router_ties_fall_back(tiny, score):
+    """Batches of >= 1024 tokens take logits from int8 slices with a certified
+    selection.  Duplicated router rows make exact ties in every token and
+    all-zero tokens make every logit equal: neither can be certified, so those
+    tokens are recomputed exactly -- and must still match the oracle bit for
+    bit, ties to the lower expert index."""
+    sh = tiny["shape"]
+    wr = tiny["wr"].copy()
+    wr[11] = wr[3]
+    wr[6] = wr[5]
+    wr[15] = wr[0]
+    wr_dev = torch.from_numpy(wr).to(DEV)
+    T = 1100
+    x = synthdata.tokens(sh, T, first=4242)
+    x[[0, 17, 1099]] = 0.0
+    y, route = _run(x, wr_dev, tiny["dev"], sh.k, score=score)
+    ref = oracle.route(x, wr, sh.k, score_fn=oracle.SCORE_SIGMOID if score == "sigmoid" else oracle.SCORE_SOFTMAX)
+    assert_route_equal(route, ref)
+    assert np.array_equal(ref["topk_idx"][0], np.arange(sh.k))  # all-zero token: the lowest indices
     assert_y_close(y, oracle_y(x, ref, range(T), tiny["get"]))
 
 
