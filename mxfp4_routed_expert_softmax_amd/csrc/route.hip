@@ -316,7 +316,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ __attribute__((aligned(16))) int8_t Bs[kSl][64 * kI8Row];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1, li = lane & 15, g = lane >> 4;
-    const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
+    // blocks go round-robin over the 8 XCDs; XCD x takes a contiguous run of
+    // tiles (token tile major), so the ~64 blocks resident on one XCD share
+    // a few x tiles and every W tile through its L2
+    const int ET = (E + 63) / 64, total = ET * ((T + 63) / 64), per = (total + 7) / 8;
+    const int id = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    if (id >= total) return;
+    const int t0 = (id / ET) * 64, e0 = (id % ET) * 64;
     // staging: thread -> (row, 16-byte piece c) of every slice; rows past the
     // end repeat the last row (their results are discarded)
     const int srow = tid >> 2, sc = tid & 3;
@@ -407,7 +413,7 @@ void launch_router_i8(int T, int E, int d, const float* x, const float* wr, cons
                       int8_t* xs, int8_t* wsl, int* xe, int* we, double* wc, double* logits, hipStream_t s)
 {
     router_slice_kernel<<<dim3(T + E), dim3(256), 0, s>>>(T, E, d, x, wr, xs, wsl, xe, we, wc);
-    router_i8_kernel<<<dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s>>>(T, E, d, xs, wsl, xe, we, bias,
+    router_i8_kernel<<<dim3(8 * ((((E + 63) / 64) * ((T + 63) / 64) + 7) / 8)), dim3(256), 0, s>>>(T, E, d, xs, wsl, xe, we, bias,
                                                                            bias_in_logits, logits);
 }
 
@@ -504,22 +510,14 @@ __global__ __launch_bounds__(1024) void topk_token_kernel(int E, int k, double* 
                                                           const float* __restrict__ wr, int d, int bias_in_logits)
 {
     __shared__ TopkLists lists;
-    __shared__ double redc[16];
-    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t = blockIdx.x;
     double* lrow = logits + (size_t)t * E;
     int32_t* idx = topk_idx + (size_t)t * k;
     float* w = topk_w + (size_t)t * k;
     if (xe) {
-        double c = 0.0;
-        for (int e = tid; e < E; e += blockDim.x) c = fmax(c, wc[e]);
-        for (int o = 32; o >= 1; o >>= 1) c = fmax(c, __shfl_xor(c, o, 64));
-        if (lane == 0) redc[wave] = c;
-        __syncthreads();
-        double cmax = 0.0;
-        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) cmax = fmax(cmax, redc[i]);
         const int ax = xe[t];
-        const double bound = ax == kZeroRow ? 0.0 : ldexp(cmax, ax);
-        if (block_topk_token(E, k, lrow, bias, bias_select_only, sigmoid, lists, nullptr, idx, w, bound)) return;
+        const double xscale = ax == kZeroRow ? 0.0 : ldexp(1.0, ax);
+        if (block_topk_token(E, k, lrow, bias, bias_select_only, sigmoid, lists, nullptr, idx, w, wc, xscale)) return;
         exact_logits_row(E, d, x + (size_t)t * d, wr, bias, bias_in_logits, lrow);
         __syncthreads();
     }

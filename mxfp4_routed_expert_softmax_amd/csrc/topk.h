@@ -172,6 +172,7 @@ struct __attribute__((aligned(16))) TopkEntry {
 struct TopkLists {
     TopkEntry list[kTopkLists][32];
     TopkEntry win[32];
+    double cmax[kTopkLists];  // certification: per-list max of the bound factors
     int ok;
 };
 
@@ -229,62 +230,93 @@ __device__ __forceinline__ void rank_winners(int nl, int k, TopkLists& L)
 // writes the k winners in order to sel_e_out (LDS, may be null), idx_out and
 // w_out (global, may be null).  Ends with a block barrier.
 //
-// With a bound (>= 0, k < E): the keys are approximations within bound of
-// the exact ones, and the selection is kept only if every gap among the best
-// k + 1 keys exceeds twice the bound (and a relative 2^-40 for the fp64
-// rounding of the keys themselves) -- then the exact keys have the same
-// winners in the same order.  Otherwise nothing is written and false comes
-// back (block-uniform).
+// Certified form (wc non-null, k < E): the keys are approximations, key e
+// within xscale * wc[e] of the exact one; with bound = xscale * max_e wc[e]
+// the selection is kept only if every gap among the best k + 1 keys exceeds
+// twice the bound (and a relative 2^-40 for the fp64 rounding of the keys
+// themselves) -- then the exact keys have the same winners in the same
+// order.  Otherwise nothing is written and false comes back (block-uniform).
+// The (k+1)-th key, for k <= 16 with 16 entries kept per list: it is either
+// kept (and then ranked k among the kept entries) or it is entry 16 of its
+// list (all k winners came from that list), so it is the best of the kept
+// rank-k entry and every list's entry 16.
 __device__ __forceinline__ bool block_topk_token(int E, int k, const double* __restrict__ lrow,
                                                  const float* __restrict__ bias, int bias_select_only, int sigmoid,
                                                  TopkLists& L, int* sel_e_out, int32_t* idx_out, float* w_out,
-                                                 double bound = -1.0)
+                                                 const double* __restrict__ wc = nullptr, double xscale = 0.0)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const bool cert = bound >= 0.0;
-    const int kk = cert ? k + 1 : k;
-    const int KL = kk <= 16 ? 16 : 32;
+    const bool cert = wc != nullptr;
+    const int KL = k <= 16 ? 16 : 32;
+    const int nk = cert ? k + 1 : k;      // ranks written to L.win
+    const bool extra = cert && KL == 16;  // entry 16 of every list kept too
     const int nl = (E + 63) / 64;  // <= waves (E <= 64 * waves): list w is wave w's
     if (wave < nl) {
         const int e = 64 * wave + lane;
         double key = -__builtin_inf();
         int id = kNoId;
+        double c = 0.0;
         if (e < E) {
             key = topk_key(lrow[e], bias, e, bias_select_only, sigmoid);
             id = e;
+            if (cert) c = wc[e];
         }
         bitonic_sort64(key, id);
-        if (lane < KL) L.list[wave][lane] = TopkEntry{key, id, 0};
+        if (lane < KL + (extra ? 1 : 0)) L.list[wave][lane] = TopkEntry{key, id, 0};
+        if (cert) {
+            c = half_max_f64(c);
+            c = fmax(c, xchg_f64<32>(c));
+            if (lane == 0) L.cmax[wave] = c;
+        }
     }
+    if (cert && threadIdx.x == 0) L.win[k] = TopkEntry{-__builtin_inf(), kNoId, 0};
     __syncthreads();
     if (wave < nl) {
         if (KL == 16)
-            rank_winners<16>(nl, kk, L);
+            rank_winners<16>(nl, nk, L);
         else
-            rank_winners<32>(nl, kk, L);
+            rank_winners<32>(nl, nk, L);
     }
     __syncthreads();
-    if (cert) {
-        if (threadIdx.x == 0) {
-            bool ok = true;
-            for (int j = 0; j + 1 < kk; ++j) {
-                const double a = L.win[j].key, b = L.win[j + 1].key;
-                ok = ok && (a - b > 2.0 * bound + 0x1p-40 * (fabs(a) + fabs(b)));
-            }
-            L.ok = ok ? 1 : 0;
-        }
-        __syncthreads();
-        if (!L.ok) return false;
-    }
+    bool ok = true;
     if (wave == 0) {
-        // softmax without a selection-only bias: the key is the weight-logit itself
         const TopkEntry w = L.win[lane & 31];
-        const int my_e = (lane < k) ? w.id : 0;
-        const double wl = (lane < k) ? ((bias_select_only || sigmoid) ? lrow[my_e] : w.key) : 0.0;
-        topk_finish(k, my_e, wl, sigmoid, !(bias_select_only || sigmoid), sel_e_out, idx_out, w_out);
+        if (cert) {
+            // lanes 0..15: the bound, and the best candidate for the (k+1)-th key
+            double c = lane < nl ? L.cmax[lane] : 0.0;
+            TopkEntry nx = (extra && lane < nl) ? L.list[lane][16] : TopkEntry{-__builtin_inf(), kNoId, 0};
+            if (lane == 0 && before(L.win[k].key, L.win[k].id, nx.key, nx.id)) nx = L.win[k];
+#define K3_NEXT_STEP(J)                                                 \
+    {                                                                   \
+        c = fmax(c, xchg_f64<J>(c));                                    \
+        const double pk = xchg_f64<J>(nx.key);                          \
+        const int pid = xchg<J>(nx.id);                                 \
+        const bool tk = before(pk, pid, nx.key, nx.id);                 \
+        nx.key = tk ? pk : nx.key;                                      \
+        nx.id = tk ? pid : nx.id;                                       \
+    }
+            K3_NEXT_STEP(8)
+            K3_NEXT_STEP(4)
+            K3_NEXT_STEP(2)
+            K3_NEXT_STEP(1)
+#undef K3_NEXT_STEP
+            const double bound = xscale * __shfl(c, 0, 64);
+            const double nxk = __shfl(nx.key, 0, 64);
+            const double b = __shfl(w.key, (lane + 1) & 63, 64);  // key of winner lane + 1
+            const double bb = lane + 1 < k ? b : nxk;
+            const bool bad = (lane < k) & !(w.key - bb > 2.0 * bound + 0x1p-40 * (fabs(w.key) + fabs(bb)));
+            ok = __ballot(bad) == 0;
+            if (lane == 0) L.ok = ok ? 1 : 0;
+        }
+        if (ok) {
+            // softmax without a selection-only bias: the key is the weight-logit itself
+            const int my_e = (lane < k) ? w.id : 0;
+            const double wl = (lane < k) ? ((bias_select_only || sigmoid) ? lrow[my_e] : w.key) : 0.0;
+            topk_finish(k, my_e, wl, sigmoid, !(bias_select_only || sigmoid), sel_e_out, idx_out, w_out);
+        }
     }
     __syncthreads();
-    return true;
+    return cert ? L.ok != 0 : true;
 }
 
 }  // namespace k3

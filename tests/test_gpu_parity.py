@@ -156,6 +156,35 @@ def test_tiny_int8_router_ties_fall_back(tiny, score):
     assert_y_close(y, oracle_y(x, ref, range(T), tiny["get"]))
 
 
+@pytest.mark.parametrize("partner", [80, 40])
+def test_int8_router_near_tie_at_k_plus_one(partner):
+    """Certified selection when the k-th and (k+1)-th experts differ by less
+    than the int8 slices resolve.  Experts 64..79 score 26, 25, ..., 11 on
+    every token (so all 16 winners come from one list of 64); the partner
+    scores 11 as well, and the higher-indexed of expert 79 and the partner
+    gets a further 2^-45 that the slices truncate away.  The exact logits
+    put that expert 16th; the sliced ones tie, so the token must fall back to
+    the exact recompute.  partner 80: the (k+1)-th is entry 16 of the
+    winners' own list; partner 40: it heads another list."""
+    E, d, k, T = 128, 256, 16, 1100
+    rng = np.random.default_rng(8080 + partner)
+    wr = np.zeros((E, d), dtype=np.float32)
+    background = [e for e in range(E) if not 64 <= e <= 79 and e != partner]
+    wr[background, 2:] = (0.1 * rng.standard_normal((len(background), d - 2))).astype(np.float32)
+    wr[64:80, 0] = np.arange(26, 10, -1, dtype=np.float32)
+    wr[partner, 0] = 11.0
+    wr[max(79, partner), 1] = np.float32(2.0 ** -45)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    x[:, 0] = 1.0
+    x[:, 1] = 1.0
+    route = k3.k3moe_route(torch.from_numpy(x).to(DEV), torch.from_numpy(wr).to(DEV), k)
+    torch.cuda.synchronize()
+    ref = oracle.route(x, wr, k)
+    expect = list(range(64, 79)) + [max(79, partner)]
+    assert all(list(r) == expect for r in ref["topk_idx"])
+    assert_route_equal(route, ref)
+
+
 def test_t0_is_a_noop(tiny):
     sh = tiny["shape"]
     x = torch.zeros((0, sh.d), dtype=torch.float32, device=DEV)
