@@ -29,6 +29,7 @@ WsLayout ws_layout(int T, int E, int k, int d, int f, int act_mode)
     L.chunk_masks = take(nch * E * sizeof(uint64_t));
     L.chunk_base = take(nch * E * sizeof(int32_t));
     L.active = take(((size_t)E + 1) * sizeof(int32_t));
+    L.passes = take((8 * (size_t)pass_stride(E) + 8) * sizeof(int32_t));
     {
         const bool i8 = use_router_i8(T, E, k, d);
         L.rsl_x = take(i8 ? (size_t)6 * T * d : 0);
@@ -245,9 +246,13 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
         a.nslots = a.P;
     } else {
         int32_t* active = reinterpret_cast<int32_t*>(ws + L.active);
-        launch_active_list(a.E, offsets, active, s);
+        const bool mx = act_mode != K3MOE_ACT_FP32;
+        int32_t* passes = reinterpret_cast<int32_t*>(ws + L.passes);
+        a.pstride = pass_stride(a.E);
+        launch_active_list(a.E, offsets, active, mx ? mx_tiles_per_pass() : 0, passes, a.pstride, s);
         a.active = active;
         a.nslots = a.E;
+        a.passes = mx ? passes : nullptr;
     }
     if (act_mode == K3MOE_ACT_FP32) {
         float* h = reinterpret_cast<float*>(ws + L.h);

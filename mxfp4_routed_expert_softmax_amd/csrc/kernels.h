@@ -17,6 +17,7 @@ struct WsLayout {
     size_t chunk_masks;  // uint64 [nch][E]          which chunk tokens chose e
     size_t chunk_base;   // int32  [nch][E]          rows of e before chunk c
     size_t active;       // int32  [E + 1]           active experts, count last
+    size_t passes;       // int32  [8*pstride + 8]   MXFP4 gate/up: pass lists per XCD
     size_t rsl_x;        // int8   [6][T][d]         int8 router: slices of x
     size_t rsl_w;        // int8   [6][E][d]         int8 router: slices of W_r
     size_t rsl_xe;       // int32  [T]               int8 router: row exponents of x
@@ -65,7 +66,12 @@ void launch_topk_group(int T, int E, int k, double* logits, const float* bias,
                        uint64_t* chunk_masks, int32_t* chunk_base, int32_t* counts,
                        int32_t* offsets, int32_t* perm_pair, int32_t* row_of_pair,
                        const TopkCert& cert, hipStream_t s);
-void launch_active_list(int E, const int32_t* offsets, int32_t* active, hipStream_t s);
+// active list; with mt > 0 also the per-XCD pass lists of FfnArgs::passes
+// (mt token tiles of 16 per pass)
+void launch_active_list(int E, const int32_t* offsets, int32_t* active, int mt, int32_t* passes,
+                        int pstride, hipStream_t s);
+int pass_stride(int E);
+int mx_tiles_per_pass();
 
 // ---- fp32-activation expert path (GEMV family) ----------------------------
 struct FfnArgs {
@@ -79,6 +85,12 @@ struct FfnArgs {
     const int32_t* row_of_pair;
     const int32_t* active;  // null: slots are sorted rows (segment heads)
     int nslots;
+    // MXFP4 gate/up with an active list: per XCD x, passes[x * pstride + j] =
+    // passes of token tiles before that XCD's j-th slot (slot x + 8j), the
+    // total last; passes[8 * pstride + x] = the XCD's slot count.  Null: one
+    // block per (slot, tile) running all of the slot's passes.
+    const int32_t* passes;
+    int pstride;
 };
 // Batches with at most kPairMajorMax token-expert pairs (and d_ff <= 8192)
 // take the pair-major path: gate/up per pair, then down with the combine

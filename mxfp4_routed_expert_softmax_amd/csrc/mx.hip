@@ -646,18 +646,16 @@ bool use_mx512(const FfnArgs& a)
            a.d % kDnTile == 0;
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_mx512_kernel(
-    FfnArgs a, const uint8_t* __restrict__ xqc, const uint8_t* __restrict__ xqs, uint8_t* __restrict__ hqc,
-    uint8_t* __restrict__ hqs, float* __restrict__ dbg_h, uint8_t* __restrict__ dbg_hc,
-    uint8_t* __restrict__ dbg_hs)
+// Passes p0 .. p1-1 of expert e (rows r_beg .., n_e tokens) against f tile
+// ftile: the block's weight scales to LDS, then one GEMM pass per <= kPassMT
+// token tiles (balanced tile counts).
+__device__ __forceinline__ void gateup_mx_item(const FfnArgs& a, int e, int r_beg, int n_e, int ftile, int p0,
+                                               int p1, uint8_t* lds, uint32_t* rowtok,
+                                               const uint8_t* __restrict__ xqc, const uint8_t* __restrict__ xqs,
+                                               uint8_t* __restrict__ hqc, uint8_t* __restrict__ hqs,
+                                               float* __restrict__ dbg_h, uint8_t* __restrict__ dbg_hc,
+                                               uint8_t* __restrict__ dbg_hs)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kMxLds];
-    __shared__ uint32_t rowtok[16 * kPassMT];
-    const int ntiles = a.f / kGuTile;
-    int slot, ftile;
-    if (!xcd_tile(blockIdx.x, a.nslots, ntiles, slot, ftile)) return;
-    int e, r_beg, n_e;
-    if (!mx_slot_expert(a, slot, e, r_beg, n_e)) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;
     const int n0 = ftile * kGuTile;
@@ -679,7 +677,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         B.bso[1] = B.bso[0] + (uint32_t)kGuTile * srow;
     }
     const int tiles = (n_e + 15) >> 4, npass = (tiles + kPassMT - 1) / kPassMT;
-    for (int p = 0; p < npass; ++p) {
+    for (int p = p0; p < p1; ++p) {
         // passes of near-equal tile counts (<= kPassMT)
         const int t0 = p * tiles / npass, t1 = (p + 1) * tiles / npass;
         const int m0 = 16 * t0, nrows = min(16 * t1, n_e) - m0, mt_n = t1 - t0;
@@ -695,16 +693,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_mx512_kernel(
-    FfnArgs a, const uint8_t* __restrict__ hqc, const uint8_t* __restrict__ hqs, float* __restrict__ o)
+// Passes p0 .. p1-1 of expert e against d tile dtile.
+__device__ __forceinline__ void down_mx_item(const FfnArgs& a, int e, int r_beg, int n_e, int dtile, int p0,
+                                             int p1, uint8_t* lds, uint32_t* rowtok,
+                                             const uint8_t* __restrict__ hqc, const uint8_t* __restrict__ hqs,
+                                             float* __restrict__ o)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kMxLds];
-    __shared__ uint32_t rowtok[16 * kPassMT];
-    const int ntiles = a.d / kDnTile;
-    int slot, dtile;
-    if (!xcd_tile(blockIdx.x, a.nslots, ntiles, slot, dtile)) return;
-    int e, r_beg, n_e;
-    if (!mx_slot_expert(a, slot, e, r_beg, n_e)) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 15, g = lane >> 4;
     const int nw = dtile * kDnTile + wave * 32;
@@ -725,7 +719,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint8_t* cbase = hqc + (size_t)r_beg * crow;
     const uint8_t* sbase = hqs + (size_t)r_beg * srow;
     const int tiles = (n_e + 15) >> 4, npass = (tiles + kPassMT - 1) / kPassMT;
-    for (int p = 0; p < npass; ++p) {
+    for (int p = p0; p < p1; ++p) {
         const int t0 = p * tiles / npass, t1 = (p + 1) * tiles / npass;
         const int m0 = 16 * t0, nrows = min(16 * t1, n_e) - m0, mt_n = t1 - t0;
         if (threadIdx.x < 16 * kPassMT) rowtok[threadIdx.x] = (uint32_t)(m0 + min((int)threadIdx.x, nrows - 1));
@@ -737,11 +731,94 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
+// Work of one gate/up block.  Without pass lists: the (slot, tile) of
+// xcd_tile and all of the slot's passes.  With them, every (slot, tile,
+// pass) is an item: the items of XCD x are its slots x + 8j in order, each
+// as tiles x passes with the passes innermost, so the passes of one (slot,
+// tile) -- the same weight rows, streamed for different tokens -- run side
+// by side on one XCD and share its L2; a heavy expert's passes no longer run
+// one after another in a single block.  Block b takes its XCD's items b/8,
+// b/8 + cap, ... (cap = the grid's blocks per XCD, sized from an estimate of
+// the count).  The down GEMM keeps one block per (slot, tile): its items are
+// a quarter as long (K = d_ff), and per-pass items measured slower there.
+constexpr int kMaxPassList = 1024 / kXcds + 8;
+
+template <typename Body>
+__device__ __forceinline__ void mx_items(const FfnArgs& a, int ntiles, int* scum, Body body)
+{
+    if (!a.passes) {
+        int slot, tile, e, r_beg, n_e;
+        if (!xcd_tile(blockIdx.x, a.nslots, ntiles, slot, tile)) return;
+        if (!mx_slot_expert(a, slot, e, r_beg, n_e)) return;
+        const int tiles = (n_e + 15) >> 4;
+        body(e, r_beg, n_e, tile, 0, (tiles + kPassMT - 1) / kPassMT);
+        return;
+    }
+    const int x = blockIdx.x % kXcds, pos0 = blockIdx.x / kXcds, cap = gridDim.x / kXcds;
+    const int nx = a.passes[kXcds * a.pstride + x];
+    for (int i = threadIdx.x; i <= nx; i += blockDim.x) scum[i] = a.passes[x * a.pstride + i];
+    __syncthreads();
+    const int total = scum[nx] * ntiles;
+    for (int pos = pos0; pos < total; pos += cap) {
+        int lo = 0, hi = nx - 1;  // the slot j with scum[j] * ntiles <= pos < scum[j + 1] * ntiles
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (scum[mid] * ntiles <= pos)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        const int npass = scum[lo + 1] - scum[lo], r = pos - scum[lo] * ntiles;
+        const int tile = r / npass, pass = r - tile * npass;
+        int e, r_beg, n_e;
+        mx_slot_expert(a, x + kXcds * lo, e, r_beg, n_e);  // an active slot
+        __syncthreads();  // the previous item is done with the LDS
+        body(e, r_beg, n_e, tile, pass, pass + 1);
+    }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gateup_mx512_kernel(
+    FfnArgs a, const uint8_t* __restrict__ xqc, const uint8_t* __restrict__ xqs, uint8_t* __restrict__ hqc,
+    uint8_t* __restrict__ hqs, float* __restrict__ dbg_h, uint8_t* __restrict__ dbg_hc,
+    uint8_t* __restrict__ dbg_hs)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMxLds];
+    __shared__ uint32_t rowtok[16 * kPassMT];
+    __shared__ int scum[kMaxPassList];
+    mx_items(a, a.f / kGuTile, scum, [&](int e, int r_beg, int n_e, int tile, int p0, int p1) {
+        gateup_mx_item(a, e, r_beg, n_e, tile, p0, p1, lds, rowtok, xqc, xqs, hqc, hqs, dbg_h, dbg_hc, dbg_hs);
+    });
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void down_mx512_kernel(
+    FfnArgs a, const uint8_t* __restrict__ hqc, const uint8_t* __restrict__ hqs, float* __restrict__ o)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kMxLds];
+    __shared__ uint32_t rowtok[16 * kPassMT];
+    int slot, tile, e, r_beg, n_e;
+    if (!xcd_tile(blockIdx.x, a.nslots, a.d / kDnTile, slot, tile)) return;
+    if (!mx_slot_expert(a, slot, e, r_beg, n_e)) return;
+    const int tiles = (n_e + 15) >> 4;
+    down_mx_item(a, e, r_beg, n_e, tile, 0, (tiles + kPassMT - 1) / kPassMT, lds, rowtok, hqc, hqs, o);
+}
+
+int mx_tiles_per_pass() { return kPassMT; }
+
+// Grid of the MXFP4 gate/up GEMM: one block per (slot, tile) without pass
+// lists; with them, per XCD its slots plus an estimate of the extra passes
+// (blocks loop over the rest).
+static int mx_grid(const FfnArgs& a, int ntiles)
+{
+    if (!a.passes) return xcd_grid(a.nslots, ntiles);
+    const int extra = (a.P + 16 * kPassMT * kXcds - 1) / (16 * kPassMT * kXcds);
+    return kXcds * ntiles * ((a.nslots + kXcds - 1) / kXcds + extra + 2);
+}
+
 void launch_gateup_mfma(const FfnArgs& a, const uint8_t* xq_codes, const uint8_t* xq_scales,
                         uint8_t* hq_codes, uint8_t* hq_scales, float* dbg_h, uint8_t* dbg_hc,
                         uint8_t* dbg_hs, hipStream_t s)
 {
-    const int grid = xcd_grid(a.nslots, (a.f + kGuTile - 1) / kGuTile);
+    const int grid = use_mx512(a) ? mx_grid(a, a.f / kGuTile) : xcd_grid(a.nslots, (a.f + kGuTile - 1) / kGuTile);
     if (use_mx512(a))
         gateup_mx512_kernel<<<dim3(grid), dim3(256), 0, s>>>(a, xq_codes, xq_scales, hq_codes, hq_scales, dbg_h,
                                                              dbg_hc, dbg_hs);

@@ -680,22 +680,42 @@ void launch_topk_group(int T, int E, int k, double* logits, const float* bias,
 
 // ---------------------------------------------------------------------------
 // Active experts in ascending id (those with at least one token); the count
-// goes to active[E].
+// goes to active[E].  With mt > 0 also the pass lists of the MXFP4 gate/up
+// GEMM: per XCD x (slot s goes to XCD s % 8) the running pass counts of its
+// slots, a slot of n tokens taking ceil(ceil(n / 16) / mt) passes.
 __global__ __launch_bounds__(1024) void active_list_kernel(int E, const int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ active)
+                                                           int32_t* __restrict__ active, int mt,
+                                                           int32_t* __restrict__ passes, int pstride)
 {
     __shared__ int wave_tot[17];
+    __shared__ int np[1024];
     const int e = threadIdx.x;
-    int flag = (e < E) ? (offsets[e + 1] > offsets[e]) : 0;
+    const int n = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+    const int flag = n > 0;
     int total;
-    int pos = block_exclusive_scan(flag, wave_tot, &total);
+    const int pos = block_exclusive_scan(flag, wave_tot, &total);
     if (flag) active[pos] = e;
     if (e == 0) active[E] = total;
+    if (mt <= 0) return;
+    if (flag) np[pos] = (((n + 15) >> 4) + mt - 1) / mt;
+    __syncthreads();
+    if (e < 8) {
+        int c = 0, j = 0;
+        for (int sl = e; sl < total; sl += 8, ++j) {
+            passes[e * pstride + j] = c;
+            c += np[sl];
+        }
+        passes[e * pstride + j] = c;
+        passes[8 * pstride + e] = j;
+    }
 }
 
-void launch_active_list(int E, const int32_t* offsets, int32_t* active, hipStream_t s)
+int pass_stride(int E) { return (E + 7) / 8 + 1; }
+
+void launch_active_list(int E, const int32_t* offsets, int32_t* active, int mt, int32_t* passes, int pstride,
+                        hipStream_t s)
 {
-    active_list_kernel<<<dim3(1), dim3(1024), 0, s>>>(E, offsets, active);
+    active_list_kernel<<<dim3(1), dim3(1024), 0, s>>>(E, offsets, active, mt, passes, pstride);
 }
 
 }  // namespace k3
