@@ -157,11 +157,14 @@ constexpr int kGuRows = 32;  // row pairs per block
 
 // PAIR: the pair-major variant for small batches -- block y serves pair
 // p = t*k + j alone (expert topk_idx[p], token t, h row p), no grouping.
-// 4 waves per SIMD: all four blocks a CU receives at d_model 7168 are resident at once
+// 4 waves per SIMD on the pair path: all four blocks a CU receives at
+// d_model 7168 are resident at once.  The grouped form (token loop, expert
+// lookups) does not fit 128 registers without spilling; it runs at 3 (its
+// scratch traffic cost more than the fourth wave gains).
 // SL (pair path only): h is written as its kSlices MX-FP8 slices (the
 // block's 32 rows are exactly one 32-value block of h) instead of fp32.
 template <int TCH, int BPL, bool PAIR, bool SL = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BPL == 1 && TCH == 1 ? 4 : 1, 8)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BPL == 1 && TCH == 1 ? (PAIR ? 4 : 3) : 1, 8)))
 void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h, uint8_t* __restrict__ hs_codes = nullptr,
                         uint8_t* __restrict__ hs_scales = nullptr)
 {
