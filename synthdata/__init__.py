@@ -56,6 +56,12 @@ K3 = LayerShape("k3", d=7168, f=2048, E=896, k=16, layer=1)
 # per block, an odd k.
 SMALL_F1536 = LayerShape("small_f1536", d=1024, f=1536, E=24, k=4, layer=2)
 SMALL_F512 = LayerShape("small_f512", d=512, f=512, E=12, k=3, layer=3)
+# The contract's limits: 1024 experts (16 top-k lists of 64) with up to 32
+# per token; and a wide layer whose d_model exceeds 256 MX blocks (two per
+# lane in the gate/up GEMV) and whose d_ff takes two blocks per lane in the
+# down GEMVs, neither a multiple of 512.
+LIMIT_E1024 = LayerShape("limit_e1024", d=256, f=128, E=1024, k=32, layer=4)
+WIDE = LayerShape("wide_d8256", d=8256, f=2560, E=8, k=2, layer=5)
 
 
 @dataclasses.dataclass(frozen=True)

@@ -320,6 +320,52 @@ def test_small_mx_split_step(small, T):
     _check_mx_split(x, ref, dbg, y, small["get"], toks, sh.d, sh.f, sh.k)
 
 
+# ------------------------------------------------------ contract limits ---
+_LIMIT_SHAPES = {sh.name: sh for sh in (synthdata.LIMIT_E1024, synthdata.WIDE)}
+_limit_layers = {}
+
+
+def _limit_layer(name):
+    if name not in _limit_layers:
+        sh = _LIMIT_SHAPES[name]
+        host = synthdata.all_experts_host(sh)
+        wr = synthdata.router_weight(sh)
+        _limit_layers[name] = dict(shape=sh, dev=_to_dev_experts(host), wr=wr,
+                                   wr_dev=torch.from_numpy(wr).to(DEV), get=host_expert_getter(sh, host))
+    return _limit_layers[name]
+
+
+# 1024 experts: k = 32 (the largest k; fp64 router at every T), k = 31 and 16
+# at 1100 tokens (the certified int8 router; k = 31 keeps 32 entries per
+# list).  The wide layer: the pair path (T = 1, 3) and the grouped path (T = 70).
+@pytest.mark.parametrize("name,k,T", [("limit_e1024", 32, 1), ("limit_e1024", 32, 70), ("limit_e1024", 32, 1100),
+                                      ("limit_e1024", 31, 1100), ("limit_e1024", 16, 1100),
+                                      ("wide_d8256", 2, 1), ("wide_d8256", 2, 3), ("wide_d8256", 2, 70)])
+def test_limit_fp32(name, k, T):
+    L = _limit_layer(name)
+    sh = L["shape"]
+    _log(f"{name} fp32 k={k} T={T}")
+    x = synthdata.tokens(sh, T, first=31 * T + k)
+    y, route = _run(x, L["wr_dev"], L["dev"], k)
+    ref = oracle.route(x, L["wr"], k)
+    assert_route_equal(route, ref)
+    toks = range(T) if T <= 128 else range(0, T, 3)
+    assert_y_close(y[list(toks)], oracle_y(x, ref, toks, L["get"]))
+
+
+@pytest.mark.parametrize("T", [3, 70])
+def test_wide_mx_split_step(T):
+    L = _limit_layer("wide_d8256")
+    sh = L["shape"]
+    _log(f"{sh.name} mx T={T}")
+    x = synthdata.tokens(sh, T, first=77 + T)
+    dbg = _dbg_buffers(T, sh.k, sh.d, sh.f)
+    y, route = _run(x, L["wr_dev"], L["dev"], sh.k, act="mxfp4", dbg=dbg)
+    ref = oracle.route(x, L["wr"], sh.k)
+    assert_route_equal(route, ref)
+    _check_mx_split(x, ref, dbg, y, L["get"], range(T), sh.d, sh.f, sh.k)
+
+
 # ----------------------------------------------------------- full layer ---
 @pytest.fixture(scope="module")
 def k3layer():
