@@ -126,22 +126,13 @@ __device__ __forceinline__ f32x4 mfma_fp4(uint4 a, uint4 b, uint32_t sa, uint32_
                                                             SEL, (int)sb);
 }
 
-// One operand row-lane's share of a K chunk: CH512 -> 64 code bytes (4 blocks)
-// and their 4 scale bytes in one word; else one 128-wide step: 16 bytes and
-// one scale byte (zeros past the row end contribute nothing).
+// One operand row-lane's share of a 512-wide K chunk: for each of the four
+// 128-wide matrix steps i, the 16 code bytes of block 4i + g (lane quarter
+// g), and the four blocks' scale bytes in one word (byte i for step i).
 struct Frag512 {
     uint4 q[4];
     uint32_t s;
 };
-
-__device__ __forceinline__ void load_frag512(const uint8_t* crow, const uint8_t* srow, int kc, int g,
-                                             Frag512& f)
-{
-    const uint8_t* cp = crow + (kc >> 1) + 64 * g;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.q[i] = ldg16(cp + 16 * i);
-    f.s = *reinterpret_cast<const uint32_t*>(srow + (kc >> 5) + 4 * g);
-}
 
 __device__ __forceinline__ void load_frag128(const uint8_t* crow, const uint8_t* srow, int kc, int g,
                                              int K, uint4& q, uint32_t& s)
@@ -423,7 +414,10 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(FfnArgs a, const uint8_t
 //
 // B = weight rows.  Their codes are buffer-loaded straight into registers
 // (each byte is used by exactly one wave) one chunk ahead of the matrix
-// work; their E8M0 scales -- 16 bytes per row and chunk, which as separate
+// work; matrix step i takes K range [128i, 128i + 128) of the chunk, so one
+// load instruction reads 64 contiguous bytes of each of 16 rows (measured
+// ~9 % faster than 16-byte pieces at a 64-byte stride, which touch twice the
+// cache lines per instruction); their E8M0 scales -- 16 bytes per row and chunk, which as separate
 // loads would cost as many cache-line requests as the codes -- are copied
 // into LDS once per block (the block's rows are contiguous, so the copy is
 // one contiguous run per weight matrix) and read from there.
@@ -448,7 +442,7 @@ __device__ __forceinline__ void b_fetch(const BSrc& b, int kc, Frag512 (&F)[2])
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) F[s].q[i] = ld_codes(b.rc[s], b.voc + 16u * i, (uint32_t)(kc >> 1));
+        for (int i = 0; i < 4; ++i) F[s].q[i] = ld_codes(b.rc[s], b.voc + 64u * i, (uint32_t)(kc >> 1));
     }
 }
 
@@ -488,15 +482,25 @@ __device__ __forceinline__ void a_issue(const ASrc& A, const uint8_t* cbase, con
 // 4g+i of row li (XOR-swizzled) and the scale word of quarter g; tile mt adds
 // 4096*mt (256*mt for the scales) -- immediate offsets of the LDS reads.
 struct AOffs {
-    uint32_t q[4], s;
+    uint32_t q[4], s, sel;
 };
+
+// The lane's four block scales (blocks g, 4+g, 8+g, 12+g of the chunk, one
+// per 128-wide step) out of the row's 16 chunk scale bytes w, as one word
+__device__ __forceinline__ uint32_t gather_scales(uint4 w, uint32_t sel)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(w.y, w.x, sel);
+    const uint32_t hi = __builtin_amdgcn_perm(w.w, w.z, sel);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
 
 __device__ __forceinline__ AOffs a_read_offsets(int li, int g)
 {
     AOffs o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o.q[i] = (uint32_t)(256 * li + 16 * ((4 * g + i) ^ li));
-    o.s = (uint32_t)(kACodes + 16 * li + 4 * g);
+    for (int i = 0; i < 4; ++i) o.q[i] = (uint32_t)(256 * li + 16 * ((4 * i + g) ^ li));
+    o.s = (uint32_t)(kACodes + 16 * li);
+    o.sel = (uint32_t)g | ((uint32_t)(4 + g) << 8) | 0x0c0c0000u;
     return o;
 }
 
@@ -506,7 +510,7 @@ __device__ __forceinline__ void a_frag(const uint8_t* st, const AOffs& o, Frag51
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) f.q[i] = *reinterpret_cast<const uint4*>(st + o.q[i] + 4096 * MT_);
-    f.s = *reinterpret_cast<const uint32_t*>(st + o.s + 256 * MT_);
+    f.s = gather_scales(*reinterpret_cast<const uint4*>(st + o.s + 256 * MT_), o.sel);
 }
 
 template <int MT_, int MT>
@@ -533,8 +537,8 @@ __device__ __forceinline__ void mma_chunk(const Frag512 (&F)[2], const BSrc& B, 
                                           const uint8_t* st, const AOffs& o, f32x4 (&c)[MT][2])
 {
     const uint8_t* bsc = lds + 2 * kAStage + (kc >> 5);
-    const uint32_t sb[2] = {*reinterpret_cast<const uint32_t*>(bsc + B.bso[0]),
-                            *reinterpret_cast<const uint32_t*>(bsc + B.bso[1])};
+    const uint32_t sb[2] = {gather_scales(*reinterpret_cast<const uint4*>(bsc + B.bso[0]), o.sel),
+                            gather_scales(*reinterpret_cast<const uint4*>(bsc + B.bso[1]), o.sel)};
     Frag512 fa;
     a_frag<0>(st, o, fa);
     mma_tiles<0, MT>(F, sb, st, o, fa, c);
@@ -672,8 +676,8 @@ __device__ __forceinline__ void gateup_mx_item(const FfnArgs& a, int e, int r_be
         const size_t wr = (size_t)e * a.f + (size_t)(n0 + 16 * wave);
         B.rc[0] = weight_rsrc(a.gc + wr * crow);
         B.rc[1] = weight_rsrc(a.uc + wr * crow);
-        B.voc = (uint32_t)li * crow + 64u * (uint32_t)g;
-        B.bso[0] = (uint32_t)(16 * wave + li) * srow + 4u * (uint32_t)g;
+        B.voc = (uint32_t)li * crow + 16u * (uint32_t)g;
+        B.bso[0] = (uint32_t)(16 * wave + li) * srow;
         B.bso[1] = B.bso[0] + (uint32_t)kGuTile * srow;
     }
     const int tiles = (n_e + 15) >> 4, npass = (tiles + kPassMT - 1) / kPassMT;
@@ -712,9 +716,9 @@ __device__ __forceinline__ void down_mx_item(const FfnArgs& a, int e, int r_beg,
     for (int s = 0; s < 2; ++s) {
         const size_t wr = (size_t)e * a.d + (size_t)(nw + 16 * s);
         B.rc[s] = weight_rsrc(a.dc + wr * crow);
-        B.bso[s] = (uint32_t)(32 * wave + 16 * s + li) * srow + 4u * (uint32_t)g;
+        B.bso[s] = (uint32_t)(32 * wave + 16 * s + li) * srow;
     }
-    B.voc = (uint32_t)li * crow + 64u * (uint32_t)g;
+    B.voc = (uint32_t)li * crow + 16u * (uint32_t)g;
     // h_q rows of the expert are contiguous: the copy bases start at its first row
     const uint8_t* cbase = hqc + (size_t)r_beg * crow;
     const uint8_t* sbase = hqs + (size_t)r_beg * srow;
