@@ -45,11 +45,16 @@ void launch_router_logits(int T, int E, int d, const float* x, const float* wr,
                           double* partials, hipStream_t s);
 // Large batches: logits from int8 slices of x and W_r (exact int32 products,
 // fp64 combination) with a rigorous per-token bound, for the certified
-// top-k.  The workspace regions rsl_* above.
-constexpr int kRouterI8MinT = 1024;
+// top-k.  The workspace regions rsl_* above; below ~1024 tokens the K axis is
+// split over router_i8_splits() blocks whose fp64 partial logits go to
+// partials and are added in split order.  Below 256 tokens slicing W_r costs
+// more than the fp64 matrix-core router takes.
+constexpr int kRouterI8MinT = 256;
 bool use_router_i8(int T, int E, int k, int d);
+int router_i8_splits(int T, int E, int d);
 void launch_router_i8(int T, int E, int d, const float* x, const float* wr, const float* bias, int bias_in_logits,
-                      int8_t* xs, int8_t* wsl, int* xe, int* we, double* wc, double* logits, hipStream_t s);
+                      int8_t* xs, int8_t* wsl, int* xe, int* we, double* wc, double* logits, double* partials,
+                      hipStream_t s);
 // What the top-k needs to certify int8 logits (xe null: exact fp64 logits)
 struct TopkCert {
     const int* xe;

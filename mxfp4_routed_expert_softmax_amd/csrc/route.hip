@@ -221,8 +221,13 @@ __global__ __launch_bounds__(256) void router_bias_kernel(long n, int E, const f
 // Against the exact x.w this is off by less than
 //   2^(a_x - 7 kSl) (kSl d 2^a_w + |w|_1)
 // (truncation of x after kSl slices, and for each slice p of x the
-// truncation of w after kSl - p slices), and the fp64 sums -- ours and the
-// oracle's sequential one -- add at most 2 (d + 8) 2^-53 2^a_x |w|_1 more.
+// truncation of w after kSl - p slices).  The fp64 sums add at most
+// (2 d + 128 + 32 S) 2^-53 2^a_x |w|_1 more, S = the K slices: the oracle's
+// sequential sum of d exact products errs by at most (d - 1) 2^-53 2^a_x
+// |w|_1; every slice of ours adds six exact level terms, each at most (l + 1)
+// 2^a_x |w|_1 over the slice (truncated slices never exceed the value), so
+// its five roundings err by at most 105 2^-53 times that, and adding the S
+// slice results by at most 21 (S - 1) 2^-53 2^a_x |w|_1.
 // wc[e] holds that bound's factor of 2^a_x for row e; the top-k of each token
 // then checks that every gap among its best k + 1 keys exceeds twice the
 // token's bound, and recomputes the token's logits exactly in fp64 where one
@@ -233,7 +238,7 @@ constexpr int kZeroRow = -100000;  // exponent marker of an all-zero row
 
 // One row per block (x rows first, then W_r rows): its exponent, its slices
 // ([kSl][rows][d] int8) and, for W_r rows, the bound factor.
-__global__ __launch_bounds__(256) void router_slice_kernel(int T, int E, int d, const float* __restrict__ x,
+__global__ __launch_bounds__(256) void router_slice_kernel(int T, int E, int d, int nsplit, const float* __restrict__ x,
                                                            const float* __restrict__ wr, int8_t* __restrict__ xs,
                                                            int8_t* __restrict__ wsl, int* __restrict__ xe,
                                                            int* __restrict__ we, double* __restrict__ wc)
@@ -291,7 +296,7 @@ __global__ __launch_bounds__(256) void router_slice_kernel(int T, int E, int d, 
             // |w|_1 rounded up (the fp64 sum of d exact terms is within d 2^-53 of it)
             const double w1 = n1 * (1.0 + 0x1p-30);
             const double c = ldexp((double)kSl * d * ldexp(1.0, m > 0.f ? a : -1000) + w1, -7 * kSl) +
-                             2.0 * (d + 8) * 0x1p-53 * w1;
+                             (2.0 * d + 128.0 + 32.0 * nsplit) * 0x1p-53 * w1;
             wc[r] = c * (1.0 + 0x1p-20);
         }
     }
@@ -310,7 +315,8 @@ typedef int i32x4v __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void router_i8_kernel(
     int T, int E, int d, const int8_t* __restrict__ xs, const int8_t* __restrict__ wsl, const int* __restrict__ xe,
-    const int* __restrict__ we, const float* __restrict__ bias, int bias_in_logits, double* __restrict__ logits)
+    const int* __restrict__ we, const float* __restrict__ bias, int bias_in_logits, double* __restrict__ logits,
+    int nsplit, double* __restrict__ part)
 {
     __shared__ __attribute__((aligned(16))) int8_t As[kSl][64 * kI8Row];
     __shared__ __attribute__((aligned(16))) int8_t Bs[kSl][64 * kI8Row];
@@ -319,15 +325,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // blocks go round-robin over the 8 XCDs; XCD x takes a contiguous run of
     // tiles (token tile major), so the ~64 blocks resident on one XCD share
     // a few x tiles and every W tile through its L2
-    const int ET = (E + 63) / 64, total = ET * ((T + 63) / 64), per = (total + 7) / 8;
+    // (the K slices of one tile are adjacent items)
+    const int ET = (E + 63) / 64, total = ET * ((T + 63) / 64) * nsplit, per = (total + 7) / 8;
     const int id = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
     if (id >= total) return;
-    const int t0 = (id / ET) * 64, e0 = (id % ET) * 64;
+    const int tile = id / nsplit, split = id - tile * nsplit;
+    const int t0 = (tile / ET) * 64, e0 = (tile % ET) * 64;
+    const int kc = d / nsplit, kb = split * kc;  // this block's K slice: [kb, kb + kc)
     // staging: thread -> (row, 16-byte piece c) of every slice; rows past the
     // end repeat the last row (their results are discarded)
     const int srow = tid >> 2, sc = tid & 3;
-    const size_t xoff = (size_t)min(t0 + srow, T - 1) * d + 16 * sc;
-    const size_t woff = (size_t)min(e0 + srow, E - 1) * d + 16 * sc;
+    const size_t xoff = (size_t)min(t0 + srow, T - 1) * d + 16 * sc + kb;
+    const size_t woff = (size_t)min(e0 + srow, E - 1) * d + 16 * sc + kb;
     const size_t xps = (size_t)T * d, wps = (size_t)E * d;
     const int8_t* xsrc = xs + xoff;
     const int8_t* wsrc = wsl + woff;
@@ -344,7 +353,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         ra[p] = *reinterpret_cast<const i32x4v*>(xsrc + p * xps);
         rb[p] = *reinterpret_cast<const i32x4v*>(wsrc + p * wps);
     }
-    for (int k0 = 0; k0 < d; k0 += 64) {
+    for (int k0 = 0; k0 < kc; k0 += 64) {
         __syncthreads();  // every wave is done with the previous step's LDS
 #pragma unroll
         for (int p = 0; p < kSl; ++p) {
@@ -355,7 +364,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         {
             // the next step's slices, in flight during this step's matrix work
             // (the last step fetches its own chunk again: branch-free)
-            const int kn = min(k0 + 64, d - 64);
+            const int kn = min(k0 + 64, kc - 64);
 #pragma unroll
             for (int p = 0; p < kSl; ++p) {
                 ra[p] = *reinterpret_cast<const i32x4v*>(xsrc + p * xps + kn);
@@ -398,8 +407,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     for (int l = kSl - 1; l >= 0; --l) sum += ldexp((double)acc[l][mi][ni][v], -7 * (l + 2));
                     const int ax = xe[t], aw = we[e];
                     double lg = (ax == kZeroRow || aw == kZeroRow) ? 0.0 : ldexp(sum, ax + aw);
-                    if (bias_in_logits) lg += (double)bias[e];
-                    logits[(size_t)t * E + e] = lg;
+                    if (nsplit > 1) {  // partial logit of this K slice, added up in slice order later
+                        part[((size_t)split * T + t) * E + e] = lg;
+                    } else {
+                        if (bias_in_logits) lg += (double)bias[e];
+                        logits[(size_t)t * E + e] = lg;
+                    }
                 }
             }
 }
@@ -409,12 +422,30 @@ bool use_router_i8(int T, int E, int k, int d)
     return T >= kRouterI8MinT && k < 32 && k < E && d % 64 == 0 && d <= 16384 && E <= 1024;
 }
 
-void launch_router_i8(int T, int E, int d, const float* x, const float* wr, const float* bias, int bias_in_logits,
-                      int8_t* xs, int8_t* wsl, int* xe, int* we, double* wc, double* logits, hipStream_t s)
+// K slices of the int8 router: the smallest power of two that gives the
+// grid about 512 blocks (at most 8; every slice whole 64-wide K steps)
+int router_i8_splits(int T, int E, int d)
 {
-    router_slice_kernel<<<dim3(T + E), dim3(256), 0, s>>>(T, E, d, x, wr, xs, wsl, xe, we, wc);
-    router_i8_kernel<<<dim3(8 * ((((E + 63) / 64) * ((T + 63) / 64) + 7) / 8)), dim3(256), 0, s>>>(T, E, d, xs, wsl, xe, we, bias,
-                                                                           bias_in_logits, logits);
+    const int tiles = ((E + 63) / 64) * ((T + 63) / 64);
+    int ns = 1;
+    while (tiles * ns < 512 && ns < 8 && (d / 64) % (2 * ns) == 0) ns *= 2;
+    return ns;
+}
+
+void launch_router_i8(int T, int E, int d, const float* x, const float* wr, const float* bias, int bias_in_logits,
+                      int8_t* xs, int8_t* wsl, int* xe, int* we, double* wc, double* logits, double* partials,
+                      hipStream_t s)
+{
+    const int ns = router_i8_splits(T, E, d);
+    router_slice_kernel<<<dim3(T + E), dim3(256), 0, s>>>(T, E, d, ns, x, wr, xs, wsl, xe, we, wc);
+    const int total = ((E + 63) / 64) * ((T + 63) / 64) * ns;
+    router_i8_kernel<<<dim3(8 * ((total + 7) / 8)), dim3(256), 0, s>>>(T, E, d, xs, wsl, xe, we, bias, bias_in_logits,
+                                                                       logits, ns, partials);
+    if (ns > 1) {
+        const long n = (long)T * E;
+        router_reduce_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(ns, n, E, partials, bias,
+                                                                                    bias_in_logits, logits);
+    }
 }
 
 int router_splits(int T, int E, int d)
