@@ -43,16 +43,20 @@ __device__ __forceinline__ float xor32(float v)
 // 16 partial sums per lane -> lane l holds the wave-wide sum of acc[l & 15].
 // Step by step the lane whose bit is set keeps the upper half and sends the
 // lower half to its partner; the order of additions is fixed.
-__device__ __forceinline__ float wave_transpose_sum16(const float (&acc)[16])
+// First step for the pair (acc[i], acc[i + 8]).
+__device__ __forceinline__ float transpose_step8(float lo, float hi)
+{
+    const bool b3 = (threadIdx.x & 63) & 8;
+    const float keep = b3 ? hi : lo, send = b3 ? lo : hi;
+    return keep + swz_xor<8>(send);
+}
+
+// The remaining steps, from the eight first-step results.
+__device__ __forceinline__ float wave_transpose_sum_from8(const float (&a8)[8])
 {
     const int lane = threadIdx.x & 63;
-    float a8[8], a4[4], a2[2];
-    const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float keep = b3 ? acc[i + 8] : acc[i], send = b3 ? acc[i] : acc[i + 8];
-        a8[i] = keep + swz_xor<8>(send);
-    }
+    float a4[4], a2[2];
+    const bool b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float keep = b2 ? a8[i + 4] : a8[i], send = b2 ? a8[i] : a8[i + 4];
@@ -68,6 +72,14 @@ __device__ __forceinline__ float wave_transpose_sum16(const float (&acc)[16])
     s += swz_xor<16>(s);
     s += xor32(s);
     return s;
+}
+
+__device__ __forceinline__ float wave_transpose_sum16(const float (&acc)[16])
+{
+    float a8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a8[i] = transpose_step8(acc[i], acc[i + 8]);
+    return wave_transpose_sum_from8(a8);
 }
 
 // Which expert does this block's slot serve?  Either the slot-th entry of the
@@ -277,11 +289,15 @@ void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h, uint8_t* __restrict__ 
 // down.  Block = 4 waves; NK waves split the f axis (one block per lane, BPL
 // per lane beyond 64*NK blocks), 4/NK teams of waves take different rows.
 // Each team owns kDnRows rows of the expert, walked in batches of R rows;
-// the weights of a batch are loaded once and applied to every token pass.
+// the weights of a batch are loaded once and applied to every token pass
+// (their scale bytes kept four to a register, and partial sums paired by the
+// first reduction step as they appear, so the d_ff = 2048 form fits 128
+// registers: four waves per SIMD without spilling).
 constexpr int kDnRows = 16;  // rows per team
 
 template <int TCH, int NK, int BPL>
-__global__ __launch_bounds__(256) void down_gemv_kernel(FfnArgs a, const float* __restrict__ hbuf,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TCH == 1 && NK == 1 && BPL == 1 ? 4 : 1, 8)))
+void down_gemv_kernel(FfnArgs a, const float* __restrict__ hbuf,
                                                         float* __restrict__ o)
 {
     constexpr int TEAMS = 4 / NK, R = 16 / TCH;
@@ -308,14 +324,18 @@ __global__ __launch_bounds__(256) void down_gemv_kernel(FfnArgs a, const float* 
 
     for (int rb = 0; rb < kDnRows; rb += R) {
         uint4 q[R][BPL];
-        uint32_t sb[R][BPL];
+        uint32_t sbp[R / 4][BPL];  // scale bytes four to a register (held across tokens)
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
+        for (int b = 0; b < BPL; ++b) {
+            uint32_t sb[R];
 #pragma unroll
-            for (int b = 0; b < BPL; ++b) {
+            for (int i = 0; i < R; ++i) {
                 q[i][b] = ld_codes(rd, coff[b], (uint32_t)(rb + i) * (uint32_t)crow);
-                sb[i][b] = ld_scale(rds, soffl[b], (uint32_t)(rb + i) * (uint32_t)srow);
+                sb[i] = ld_scale(rds, soffl[b], (uint32_t)(rb + i) * (uint32_t)srow);
             }
+#pragma unroll
+            for (int j = 0; j < R / 4; ++j)
+                sbp[j][b] = sb[4 * j] | (sb[4 * j + 1] << 8) | (sb[4 * j + 2] << 16) | (sb[4 * j + 3] << 24);
         }
         for (int t0 = 0; t0 < n_e; t0 += TCH) {
             float hr[BPL][TCH][32];
@@ -329,22 +349,37 @@ __global__ __launch_bounds__(256) void down_gemv_kernel(FfnArgs a, const float* 
 #pragma unroll
                     for (int i = 0; i < 32; ++i) hr[b][tt][i] = tmp[b][i];
             }
-            float acc[16];
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                float s[TCH];
+            auto row_dot = [&](int i, float (&s)[TCH]) {
 #pragma unroll
                 for (int tt = 0; tt < TCH; ++tt) s[tt] = 0.f;
 #pragma unroll
                 for (int b = 0; b < BPL; ++b) {
                     uint4 qq = q[i][b];
+                    uint32_t sp = sbp[i >> 2][b];
                     opaque(qq);
-                    dot32_multi<TCH>(qq, e8m0_f32(sb[i][b]), hr[b], s);
+                    asm volatile("" : "+v"(sp));
+                    dot32_multi<TCH>(qq, e8m0_f32((sp >> (8 * (i & 3))) & 0xffu), hr[b], s);
                 }
+            };
+            float a8[8];
 #pragma unroll
-                for (int tt = 0; tt < TCH; ++tt) acc[tt * R + i] = s[tt];
+            for (int j = 0; j < 8; ++j) {
+                float lo, hi;
+                if (TCH == 1) {
+                    float s0[TCH], s1[TCH];
+                    row_dot(j, s0);
+                    row_dot(j + 8, s1);
+                    lo = s0[0];
+                    hi = s1[TCH - 1];
+                } else {
+                    float s2[TCH];
+                    row_dot(j, s2);
+                    lo = s2[0];
+                    hi = s2[TCH - 1];
+                }
+                a8[j] = transpose_step8(lo, hi);
             }
-            const float v = wave_transpose_sum16(acc);
+            const float v = wave_transpose_sum_from8(a8);
             const int tt = (lane & 15) / R, i = (lane & 15) % R;
             if (NK == 1) {
                 if (live && lane < 16 && t0 + tt < n_e)
