@@ -141,6 +141,13 @@ int k3moe_workspace_size(const k3moe_dims *dims, int act_mode, size_t *bytes);
  *   perm_pair   int32 [T*k]   row -> pair t*k+j; rows grouped by expert in
  *                             ascending expert id, tokens ascending inside
  *   row_of_pair int32 [T*k]   inverse of perm_pair
+ * The selection is the one the exact logits x.w_e (+ bias) make.  Batches of
+ * 256 tokens or more (k < 32, k < E, d_model % 64 == 0) take the logits from
+ * int8 slices of x and w_router with a rigorous per-token error bound; a
+ * token whose best k + 1 keys are not separated by more than twice that
+ * bound has its logits recomputed exactly in fp64 before selecting, so ties
+ * and near-ties resolve as on exact logits.  topk_w is then computed from the
+ * sliced logits (within ~1e-8 relative of the exact-logit weights).
  * ws: device workspace of at least k3moe_workspace_size() bytes, 256-aligned. */
 int k3moe_route(const k3moe_dims *dims, const float *x, const float *w_router,
                 const float *bias, int bias_mode, int score_fn,
