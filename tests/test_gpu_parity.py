@@ -185,6 +185,51 @@ def test_int8_router_near_tie_at_k_plus_one(partner):
     assert_route_equal(route, ref)
 
 
+def _graph_replays_match_eager(xs, wr_dev, experts, k, act="fp32"):
+    """k3moe_forward captured once in a HIP graph, then replayed for each
+    input in xs (copied into the captured input buffer), with an eager call
+    on another input between replays: every replay must equal an eager call
+    on the same input bit for bit (outputs and all routing buffers).  The
+    library allocates nothing and issues no memset, so every node is a
+    kernel."""
+    gx = xs[0].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    fw = k3.Forward(gx, wr_dev, experts, k, act_mode=act, stream=s)
+    with torch.cuda.stream(s):
+        fw()  # first call outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fw()
+    torch.cuda.synchronize()
+    eager = k3.Forward(xs[0], wr_dev, experts, k, act_mode=act)
+    n = len(xs)
+    for r in range(n):
+        gx.copy_(xs[r])
+        g.replay()
+        torch.cuda.synchronize()
+        y_g = fw.y.clone()
+        route_g = {name: t.clone() for name, t in fw.route.items()}
+        eager.set_x(xs[(r + 1) % n])
+        eager()
+        torch.cuda.synchronize()
+        eager.set_x(xs[r])
+        y_e = eager().clone()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_e), f"replay {r}: y differs from the eager call"
+        for name in route_g:
+            assert torch.equal(route_g[name], eager.route[name]), f"replay {r}: {name} differs"
+
+
+@pytest.mark.parametrize("T,act", [(1, "fp32"), (40, "fp32"), (300, "mxfp4"), (1100, "fp32")])
+def test_tiny_graph_replay(tiny, T, act):
+    sh = tiny["shape"]
+    _log(f"tiny graph replay T={T} {act}")
+    xs = [torch.from_numpy(synthdata.tokens(sh, T, first=6000 + 10 * T + r * T)).to(DEV) for r in range(4)]
+    _graph_replays_match_eager(xs, tiny["wr_dev"], tiny["dev"], sh.k, act)
+
+
 def test_t0_is_a_noop(tiny):
     sh = tiny["shape"]
     x = torch.zeros((0, sh.d), dtype=torch.float32, device=DEV)
@@ -400,6 +445,13 @@ def test_k3_sigmoid_router_select_only_bias(k3layer, T):
     assert_route_equal(route, ref)
     toks = [0] if T == 1 else [0, 17, 63]
     assert_y_close(y[toks], oracle_y(x, ref, toks, k3layer["get"]))
+
+
+def test_k3_decode_graph_replay(k3layer):
+    sh = k3layer["shape"]
+    _log("k3 decode graph replay")
+    xs = [torch.from_numpy(synthdata.tokens(sh, 1, first=7000 + r)).to(DEV) for r in range(4)]
+    _graph_replays_match_eager(xs, k3layer["wr_dev"], k3layer["dev"], sh.k)
 
 
 def test_k3_decode_t1(k3layer):
