@@ -26,45 +26,11 @@ __device__ __forceinline__ f32x2 fp4x2_scaled(uint32_t w, float scale)
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, SEL);
 }
 
-// acc += sum over the 8 codes of w (elements 0..7) times xs[0..7].
-__device__ __forceinline__ float dot8_fp4(uint32_t w, float scale, const float* xs, float acc)
-{
-    f32x2 a = fp4x2_scaled<0>(w, scale);
-    f32x2 b = fp4x2_scaled<1>(w, scale);
-    f32x2 c = fp4x2_scaled<2>(w, scale);
-    f32x2 d = fp4x2_scaled<3>(w, scale);
-    acc = __builtin_fmaf(a.x, xs[0], acc);
-    acc = __builtin_fmaf(a.y, xs[1], acc);
-    acc = __builtin_fmaf(b.x, xs[2], acc);
-    acc = __builtin_fmaf(b.y, xs[3], acc);
-    acc = __builtin_fmaf(c.x, xs[4], acc);
-    acc = __builtin_fmaf(c.y, xs[5], acc);
-    acc = __builtin_fmaf(d.x, xs[6], acc);
-    acc = __builtin_fmaf(d.y, xs[7], acc);
-    return acc;
-}
-
-// acc += (one 32-element MX block: 16 code bytes in q, scale) . xs[0..31]
-__device__ __forceinline__ float dot32_fp4(uint4 q, float scale, const float* xs, float acc)
-{
-    acc = dot8_fp4(q.x, scale, xs + 0, acc);
-    acc = dot8_fp4(q.y, scale, xs + 8, acc);
-    acc = dot8_fp4(q.z, scale, xs + 16, acc);
-    acc = dot8_fp4(q.w, scale, xs + 24, acc);
-    return acc;
-}
-
 // Overflow-free SiLU in fp32: z / (1 + e^-z) (e^-z -> inf gives -0 for very
 // negative z, the correct limit).
 __device__ __forceinline__ float silu_f32(float z)
 {
     return z / (1.0f + expf(-z));
-}
-
-template <typename T>
-__device__ __forceinline__ T shfl_xor(T v, int m, int width = kWave)
-{
-    return __shfl_xor(v, m, width);
 }
 
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p)
