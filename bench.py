@@ -58,7 +58,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the layer is measured on one GPU: --gpus must be 1 (sharding across GPUs is described, not built)"}))
         sys.exit(2)
     import torch
     import synthdata
