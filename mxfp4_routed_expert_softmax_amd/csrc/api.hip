@@ -6,7 +6,6 @@
 // guessing: fiv.co.kr "kimi-k3-in-c deep dive", the study-plan row on
 // correctness and reproducibility).  All checks run before the first HIP call.
 #include <string.h>
-#include <algorithm>
 #include <atomic>
 #include "k3moe.h"
 #include "kernels.h"
@@ -24,10 +23,8 @@ WsLayout ws_layout(int T, int E, int k, int d, int f, int act_mode)
     auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
     L.logits = take((size_t)T * E * sizeof(double));
     {
-        // the fp64 router's splits, or the int8 router's (it falls back to
-        // the fp64 one for unaligned x or W_r)
-        int ns = router_splits(T, E, d);
-        if (use_router_i8(T, E, k, d)) ns = std::max(ns, router_i8_splits(T, E, d));
+        // K splits of whichever router these dimensions take
+        const int ns = use_router_i8(T, E, k, d) ? router_i8_splits(T, E, d) : router_splits(T, E, d);
         L.partials = take(ns > 1 ? (size_t)ns * T * E * sizeof(double) : 0);
     }
     L.chunk_masks = take(nch * E * sizeof(uint64_t));
@@ -196,7 +193,7 @@ static void enqueue_route(const k3moe_dims* dm, const float* x, const float* w_r
     double* logits = reinterpret_cast<double*>(ws + L.logits);
     const int bias_in_logits = bias_mode == K3MOE_BIAS_LOGITS;
     TopkCert cert{nullptr, nullptr, x, w_router, dm->d_model, bias_in_logits};
-    if (use_router_i8(dm->T, dm->E, dm->k, dm->d_model) && aligned(x, 16) && aligned(w_router, 16)) {
+    if (use_router_i8(dm->T, dm->E, dm->k, dm->d_model)) {  // x, w_router 16-B aligned: checked above
         int* xe = reinterpret_cast<int*>(ws + L.rsl_xe);
         double* wc = reinterpret_cast<double*>(ws + L.rsl_wc);
         launch_router_i8(dm->T, dm->E, dm->d_model, x, w_router, bias, bias_in_logits,
