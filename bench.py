@@ -30,6 +30,8 @@ TRAFFIC_SOURCES = ["mxfp4_routed_expert_softmax_amd/csrc/" + f for f in
 FFN_KERNELS = ("gateup_", "down_", "combine_", "quantize_rows", "zero_kernel", "active_list")
 MXFP4_PEAK_TFLOPS = 10100.0  # dense MXFP4 matrix peak
 EV_EVERY_DECODE = 10  # one-token steps per event-marked step (others: every step)
+MIN_EV_SAMPLES = 10   # event-marked steps per measurement, whatever --steps is
+PREFILL_WORKLOAD = "k3_prefill_t4096"  # timed after the headline workload, same run
 
 
 def log(*a):
@@ -49,6 +51,9 @@ def parse():
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="also time steps with a read of this many MiB between them (caches cold; "
                          "informational, reported under 'flushed')")
+    ap.add_argument("--prefill-steps", type=int, default=10,
+                    help="timed steps of the 4096-token MXFP4 prefill reported under 'prefill' "
+                         "(0 disables it; only with the headline decode workload)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB three times "
                          "(reference kernel for hardware byte counters; not part of the step)")
@@ -73,91 +78,24 @@ def main():
     t0 = time.time()
     experts = synthdata.upload_experts(sh, dev)
     wr = torch.from_numpy(synthdata.router_weight(sh)).to(dev)
-    bias = torch.from_numpy(synthdata.zipf_bias(sh)).to(dev) if wl.zipf_bias else None
-    bias_mode = "logits" if wl.zipf_bias else "none"
-    # distinct seeded batches, resident in HBM before timing
-    nbatch = 1000 if T == 1 else max(1, min(8, 1000 // T))
-    xs = [torch.from_numpy(synthdata.tokens(sh, T, first=i * T)).to(dev) for i in range(nbatch)]
     torch.cuda.synchronize()
-    log(f"inputs resident in {time.time() - t0:.1f}s ({nbatch} batches)")
+    log(f"layer resident in {time.time() - t0:.1f}s")
 
-    fw = k3.Forward(xs[0], wr, experts, sh.k, bias, bias_mode, wl.act_mode)
-    stream = torch.cuda.current_stream()
-    route = fw.route
+    m = measure(k3, synthdata, torch, dev, wl, experts, wr, args.steps, args.warmup, args.graph)
+    fw, xs, nbatch, stream = m["fw"], m["xs"], m["nbatch"], m["stream"]
+    ms_per_step, tokens_per_s, roofline = m["ms_per_step"], m["tokens_per_s"], m["roofline"]
+    n_active, bias_mode, graph = m["n_active"], m["bias_mode"], m["graph"]
 
-    def step(i, ev=None):
-        fw.set_x(xs[i % nbatch])
-        if ev is None:
-            fw()  # k3moe_forward: the whole layer in one C call
-        else:
-            # the same work as two calls, HIP events on this stream around
-            # the expert-FFN stage (k3moe_ffn)
-            fw.run_route()
-            ev[0].record(stream)
-            fw.run_ffn()
-            ev[1].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    graph = None
-    if args.graph:
-        gx = xs[0].clone()
-        fw.set_x(gx)
-        s = torch.cuda.Stream()
-        s.wait_stream(stream)
-        with torch.cuda.stream(s):
-            fw.stream = s
-            fw()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=s):
-            fw()
-        fw.stream = None
-        torch.cuda.synchronize()
-
-    # timed region: K steps; event-marked steps carry events around their
-    # expert-FFN stage.  An event record costs a few microseconds of stream
-    # time, so one-token steps (~0.1 ms) are marked one in EV_EVERY_DECODE.
-    EV_EVERY = EV_EVERY_DECODE if T == 1 else 1
-    nev = (args.steps + EV_EVERY - 1) // EV_EVERY
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    if graph is None:
-        for i in range(args.steps):
-            step(i, evs[i // EV_EVERY] if i % EV_EVERY == 0 else None)
-    else:
-        for i in range(args.steps):
-            gx.copy_(xs[i % nbatch], non_blocking=True)
-            graph.replay()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    ms_per_step = elapsed * 1e3 / args.steps
-    tokens_per_s = T * args.steps / elapsed
-
-    # bytes of the active experts, from this run's own counts (last step)
-    counts = route["counts"].cpu().numpy()
-    n_active = int((counts > 0).sum())
-    expert_bytes = n_active * sh.expert_bytes
-    act_bytes = 2 * T * sh.d * 4  # x read, y written
-    roofline = None
-    if graph is None:
-        ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-        achieved = (expert_bytes + act_bytes) / (ffn_ms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
-                    "kernel": "expert FFN stage (every kernel k3moe_ffn launches; decode: gate/up GEMV "
-                              "with SwiGLU + down GEMV with the fused combine)",
-                    "bytes_per_launch": expert_bytes + act_bytes, "avg_ms": round(ffn_ms, 5)}
-        # the whole layer per step (router weights + active experts + x, y) over the timed step time
-        layer_bytes = sh.E * sh.d * 4 + expert_bytes + act_bytes
-        roofline["layer"] = {"bytes_per_step": layer_bytes,
-                             "frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    if wl.act_mode == "mxfp4" and roofline is not None:
-        flops = 2.0 * 3 * sh.d * sh.f * T * sh.k
-        roofline["mfma_frac"] = round(flops / (roofline["avg_ms"] * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS, 4)
+    prefill = None
+    if args.prefill_steps > 0 and wl.name == "k3_decode_t1" and not args.graph:
+        pw = synthdata.WORKLOADS[PREFILL_WORKLOAD]
+        log(f"prefill block: {pw.name}")
+        pm = measure(k3, synthdata, torch, dev, pw, experts, wr, args.prefill_steps, 3, False)
+        prefill = {"workload": pw.name, "T": pw.T, "activations": pw.act_mode, "steps": args.prefill_steps,
+                   "warmup": 3, "ms_per_step": round(pm["ms_per_step"], 5),
+                   "tokens_per_s": round(pm["tokens_per_s"], 1), "roofline": pm["roofline"],
+                   "active_experts_last_step": pm["n_active"]}
+        del pm
 
     flushed = None
     if args.flush_mib > 0:
@@ -213,9 +151,107 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if prefill is not None:
+        out["prefill"] = prefill
     if flushed is not None:
         out["flushed"] = flushed
     print(json.dumps(out), flush=True)
+
+
+def measure(k3, synthdata, torch, dev, wl, experts, wr, steps, warmup, use_graph):
+    """Time `steps` steps of workload wl (after `warmup`), inputs resident.
+    Every ev_every-th step issues k3moe_route and k3moe_ffn as two calls with
+    HIP events on the launch stream around the expert-FFN stage; the others
+    issue k3moe_forward.  At least MIN_EV_SAMPLES steps carry events."""
+    sh, T = wl.shape, wl.T
+    bias = torch.from_numpy(synthdata.zipf_bias(sh)).to(dev) if wl.zipf_bias else None
+    bias_mode = "logits" if wl.zipf_bias else "none"
+    # distinct seeded batches, resident in HBM before timing
+    nbatch = 1000 if T == 1 else max(1, min(8, 1000 // T))
+    xs = [torch.from_numpy(synthdata.tokens(sh, T, first=i * T)).to(dev) for i in range(nbatch)]
+    torch.cuda.synchronize()
+
+    fw = k3.Forward(xs[0], wr, experts, sh.k, bias, bias_mode, wl.act_mode)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        fw.set_x(xs[i % nbatch])
+        if ev is None:
+            fw()  # k3moe_forward: the whole layer in one C call
+        else:
+            # the same work as two calls, HIP events on this stream around
+            # the expert-FFN stage (k3moe_ffn)
+            fw.run_route()
+            ev[0].record(stream)
+            fw.run_ffn()
+            ev[1].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    graph = None
+    if use_graph:
+        gx = xs[0].clone()
+        fw.set_x(gx)
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            fw.stream = s
+            fw()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            fw()
+        fw.stream = None
+        torch.cuda.synchronize()
+
+    # timed region: K steps; event-marked steps carry events around their
+    # expert-FFN stage.  An event record costs a few microseconds of stream
+    # time, so one-token steps (~0.1 ms) are marked one in EV_EVERY_DECODE
+    # (more often when there are fewer than MIN_EV_SAMPLES * EV_EVERY_DECODE).
+    ev_every = max(1, min(EV_EVERY_DECODE if T == 1 else 1, steps // MIN_EV_SAMPLES))
+    nev = (steps + ev_every - 1) // ev_every
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    if graph is None:
+        for i in range(steps):
+            step(i, evs[i // ev_every] if i % ev_every == 0 else None)
+    else:
+        for i in range(steps):
+            gx.copy_(xs[i % nbatch], non_blocking=True)
+            graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / steps
+    tokens_per_s = T * steps / elapsed
+
+    # bytes of the active experts, from this run's own counts (last step)
+    counts = fw.route["counts"].cpu().numpy()
+    n_active = int((counts > 0).sum())
+    expert_bytes = n_active * sh.expert_bytes
+    act_bytes = 2 * T * sh.d * 4  # x read, y written
+    roofline = None
+    if graph is None:
+        ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        achieved = (expert_bytes + act_bytes) / (ffn_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
+                    "kernel": "expert FFN stage (every kernel k3moe_ffn launches)",
+                    "bytes_per_launch": expert_bytes + act_bytes, "avg_ms": round(ffn_ms, 5),
+                    "event_samples": len(evs)}
+        # the whole layer per step (router weights + active experts + x, y) over the timed step time
+        layer_bytes = sh.E * sh.d * 4 + expert_bytes + act_bytes
+        roofline["layer"] = {"bytes_per_step": layer_bytes,
+                             "frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if wl.act_mode == "mxfp4":
+            flops = 2.0 * 3 * sh.d * sh.f * T * sh.k
+            roofline["flops_per_launch"] = flops
+            roofline["mfma_frac"] = round(flops / (ffn_ms * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS, 4)
+    return dict(fw=fw, xs=xs, nbatch=nbatch, stream=stream, ms_per_step=ms_per_step,
+                tokens_per_s=tokens_per_s, roofline=roofline, n_active=n_active, bias_mode=bias_mode,
+                graph=graph)
 
 
 def measured_traffic(workload):
@@ -268,9 +304,35 @@ def cpu_baseline(sh, wl, budget_s):
         tok += 1
         if len(cache) > 256:
             cache.clear()
-    return {"value": round(done / spent, 4), "unit": "tokens/s", "cores": oracle.num_threads(),
+    threads = oracle.num_threads()
+    # one more token on a single thread, for context
+    oracle.set_num_threads(1)
+    x = synthdata.tokens(sh, 1, first=tok)
+    r = oracle.route(x, wr, sh.k, bias, bm)
+    for e in r["topk_idx"][0]:
+        if int(e) not in cache:
+            cache[int(e)] = synthdata.expert(sh, int(e))
+    t0 = time.perf_counter()
+    r = oracle.route(x, wr, sh.k, bias, bm)
+    oracle.token_forward(x[0], r["topk_idx"][0], r["topk_w"][0], lambda e: cache[int(e)], act_mode=wl.act_mode)
+    one_thread_s = time.perf_counter() - t0
+    oracle.set_num_threads(threads)
+    return {"value": round(done / spent, 4), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{done} single tokens of {wl.name} (full layer per token, fp64), {spent:.1f}s"}
+            "sample": f"{done} single tokens of {wl.name} (full layer per token, fp64), {spent:.1f}s",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "one_thread_s_per_token": round(one_thread_s, 3)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

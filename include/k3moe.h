@@ -49,7 +49,8 @@ extern "C" {
 #define K3MOE_OK          0
 #define K3MOE_EINVAL     -1  /* bad dimension, null or misaligned pointer    */
 #define K3MOE_EWORKSPACE -2  /* workspace missing or smaller than required   */
-#define K3MOE_ENOTSUP    -3  /* unknown mode, E > 1024, k > 32, not gfx950   */
+#define K3MOE_ENOTSUP    -3  /* unknown mode, E > 1024, k > 32, d_model or
+                                d_ff > 16384, not gfx950                     */
 #define K3MOE_EHIP       -4  /* a HIP call or launch failed; see last_hip_error */
 
 /* ---- modes --------------------------------------------------------------- */
@@ -87,16 +88,21 @@ typedef struct {
     int32_t T;        /* tokens, >= 0                                         */
     int32_t E;        /* routed experts, 1..1024                              */
     int32_t k;        /* experts per token, 1..min(E, 32)                     */
-    int32_t d_model;  /* > 0, multiple of 32                                  */
-    int32_t d_ff;     /* > 0, multiple of 32                                  */
+    int32_t d_model;  /* 32..16384, multiple of 32 (above 16384: ENOTSUP)     */
+    int32_t d_ff;     /* 32..16384, multiple of 32 (above 16384: ENOTSUP)     */
 } k3moe_dims;
 
 /* One MX matrix [rows][cols] (blocks of 32 along cols, the reduction axis):
  *   codes  : uint8 [rows][cols/2], element 2i in the low nibble of byte i,
  *            element 2i+1 in the high nibble; 16-byte aligned
- *   scales : uint8 [rows][cols/32], E8M0 (255 = NaN is outside the contract)
+ *   scales : uint8 [rows][cols/32], E8M0 scale bytes 0..252
  * Rows are contiguous with no padding: a matrix of P values takes
- * P/2 + P/32 bytes (0.53125 B/param, the pages' per-expert byte count). */
+ * P/2 + P/32 bytes (0.53125 B/param, the pages' per-expert byte count).
+ * Scale bytes 253 and 254 are outside the contract: the kernels decode and
+ * accumulate in fp32, where code 6 at 2^126 or 2^127 (and the sums of such
+ * values) overflow; byte 255 is the format's NaN.  Byte 0 is the subnormal
+ * scale 2^-127 and is decoded exactly.  Nothing checks the bytes on the
+ * device: out-of-contract weights give unspecified y. */
 typedef struct {
     const uint8_t *codes;
     const uint8_t *scales;
@@ -141,12 +147,15 @@ int k3moe_workspace_size(const k3moe_dims *dims, int act_mode, size_t *bytes);
  *   perm_pair   int32 [T*k]   row -> pair t*k+j; rows grouped by expert in
  *                             ascending expert id, tokens ascending inside
  *   row_of_pair int32 [T*k]   inverse of perm_pair
- * The selection is the one the exact logits x.w_e (+ bias) make.  Batches of
+ * The selection is the one the fp64 router makes: logits are fp64 sums of
+ * the exact fp32 x fp32 products (within ~d 2^-53 max|x||w| of the exact dot
+ * product; equal router rows give equal logits), plus the bias.  Batches of
  * 256 tokens or more (k < 32, k < E, d_model % 64 == 0) take the logits from
  * int8 slices of x and w_router with a rigorous per-token error bound; a
  * token whose best k + 1 keys are not separated by more than twice that
- * bound has its logits recomputed exactly in fp64 before selecting, so ties
- * and near-ties resolve as on exact logits.  topk_w is then computed from the
+ * bound has its logits recomputed in fp64 before selecting (one wave per
+ * expert row: the same guarantee, another summation order), so exact ties
+ * still resolve to the lower expert index.  topk_w is then computed from the
  * sliced logits (within ~1e-8 relative of the exact-logit weights).
  * ws: device workspace of at least k3moe_workspace_size() bytes, 256-aligned. */
 int k3moe_route(const k3moe_dims *dims, const float *x, const float *w_router,

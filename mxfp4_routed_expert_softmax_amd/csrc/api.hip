@@ -75,6 +75,9 @@ static int check_dims(const k3moe_dims* dm)
         ((int64_t)1 << 40))
         return K3MOE_EINVAL;  // row offsets must fit the kernels' index arithmetic
     if (dm->E > 1024 || dm->k > 32) return K3MOE_ENOTSUP;
+    // the fp32-activation GEMVs give each lane at most two MX blocks of a
+    // row (256 lanes x 2 x 32 values): wider reduction axes are refused
+    if (dm->d_model > kMaxDim || dm->d_ff > kMaxDim) return K3MOE_ENOTSUP;
     return K3MOE_OK;
 }
 
@@ -371,7 +374,7 @@ const char* k3moe_status_string(int status)
         case K3MOE_OK: return "ok";
         case K3MOE_EINVAL: return "invalid argument (dimension, null or misaligned pointer)";
         case K3MOE_EWORKSPACE: return "workspace missing or too small";
-        case K3MOE_ENOTSUP: return "not supported (mode, E > 1024, k > 32, or device is not gfx950)";
+        case K3MOE_ENOTSUP: return "not supported (mode, E > 1024, k > 32, d_model or d_ff > 16384, or device is not gfx950)";
         case K3MOE_EHIP: return "HIP error (see k3moe_last_hip_error)";
         default: return "unknown status";
     }

@@ -538,7 +538,7 @@ static void gateup_dispatch(const FfnArgs& a, float* h, hipStream_t s)
     if (nb <= 256)
         gateup_gemv_kernel<TCH, 1, PAIR><<<grid, dim3(256), 0, s>>>(a, h);
     else
-        gateup_gemv_kernel<TCH, 2, PAIR><<<grid, dim3(256), 0, s>>>(a, h);  // d <= 16384 (checked)
+        gateup_gemv_kernel<TCH, 2, PAIR><<<grid, dim3(256), 0, s>>>(a, h);  // d <= kMaxDim: wider rows are refused by the ABI
 }
 
 bool use_pair_path(const FfnArgs& a) { return a.P <= kPairMajorMax && a.f <= 8192; }
@@ -593,7 +593,7 @@ static void down_dispatch_nk(const FfnArgs& a, const float* h, float* o, hipStre
     if (nb <= 64 * NK)
         down_gemv_kernel<TCH, NK, 1><<<grid, dim3(256), 0, s>>>(a, h, o);
     else
-        down_gemv_kernel<TCH, NK, 2><<<grid, dim3(256), 0, s>>>(a, h, o);  // f <= 16384 (checked)
+        down_gemv_kernel<TCH, NK, 2><<<grid, dim3(256), 0, s>>>(a, h, o);  // f <= kMaxDim: wider rows are refused by the ABI
 }
 
 template <int TCH>

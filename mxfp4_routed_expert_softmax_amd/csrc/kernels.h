@@ -9,6 +9,8 @@ namespace k3 {
 
 // Tokens per permutation chunk: one bit per token in a 64-bit mask.
 constexpr int kChunk = 64;
+// Largest d_model and d_ff: the GEMVs cover 512 MX blocks of a row.
+constexpr int kMaxDim = 16384;
 
 // Workspace carve-up (byte offsets from the 256-aligned workspace base).
 struct WsLayout {

@@ -419,7 +419,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 bool use_router_i8(int T, int E, int k, int d)
 {
-    return T >= kRouterI8MinT && k < 32 && k < E && d % 64 == 0 && d <= 16384 && E <= 1024;
+    return T >= kRouterI8MinT && k < 32 && k < E && d % 64 == 0 && d <= kMaxDim && E <= 1024;
 }
 
 // K slices of the int8 router: the smallest power of two that gives the

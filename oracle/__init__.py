@@ -63,6 +63,7 @@ def lib():
         L.k3o_gateup.argtypes = [I, I, P, P, P, P, P, P, P, P]
         L.k3o_down.argtypes = [I, I, P, P, P, P]
         L.k3o_num_threads.restype = I
+        L.k3o_set_num_threads.argtypes = [I]
         _lib = L
     return _lib
 
@@ -91,6 +92,10 @@ def silu(z: float) -> float:
 
 def num_threads() -> int:
     return lib().k3o_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().k3o_set_num_threads(int(n))
 
 
 def mx_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
@@ -277,3 +282,53 @@ def token_forward(x_t: np.ndarray, experts_t, w_t, get_expert, act_mode: str = "
     if keep is not None:
         keep.update(x_used=x, h=hs, h_q=hq)
     return y
+
+
+def layer_forward(x: np.ndarray, route: dict, tokens, get_expert, act_mode: str = "fp32",
+                  h_override=None, keep: dict | None = None) -> np.ndarray:
+    """y rows (fp64) of the given tokens: for each, exactly the sum
+    token_forward forms (y_t = sum_j w_j * FFN_{e_j}(x_t), j ascending, from
+    y = 0), but the experts are visited once each, in ascending id, for all of
+    their pairs among these tokens, so that each expert's weights are fetched
+    once.  ``get_expert`` is called with the needed ids in ascending order.
+    ``h_override(t)`` (optional) returns the k h vectors of token t that
+    replace the oracle's own h, as in token_forward.  ``keep`` (optional
+    dict) receives keep["h"][(t, j)], the oracle's own h of each pair (from
+    the quantised x in "mxfp4" mode), computed even where h_override
+    replaces it."""
+    if act_mode not in ("fp32", "mxfp4"):
+        raise ValueError("unknown activation mode")
+    tokens = [int(t) for t in tokens]
+    idx, w = route["topk_idx"], route["topk_w"]
+    k = idx.shape[1]
+    xin = {}
+    for t in tokens:
+        xin[t] = (mx_roundtrip(np.asarray(x[t], np.float32)) if act_mode == "mxfp4"
+                  else np.asarray(x[t], np.float64))
+    by_expert = {}
+    for t in tokens:
+        for j in range(k):
+            by_expert.setdefault(int(idx[t, j]), []).append((t, j))
+    hov = {t: h_override(t) for t in tokens} if h_override is not None else None
+    o = {}
+    for e in sorted(by_expert):
+        ex = get_expert(e)
+        for t, j in by_expert[e]:
+            h = None
+            if hov is None or keep is not None:
+                h = gateup(xin[t], ex["gate"], ex["up"])
+                if keep is not None:
+                    keep.setdefault("h", {})[(t, j)] = h
+            if hov is not None:
+                h = np.asarray(hov[t][j])
+            if act_mode == "mxfp4":
+                c, s = mx_quantize(h.reshape(1, -1))
+                h = mx_dequant(c, s).reshape(-1)
+            o[(t, j)] = down(h, ex["down"])
+    out = np.empty((len(tokens), x.shape[1]), np.float64)
+    for i, t in enumerate(tokens):
+        y = np.zeros(x.shape[1], np.float64)
+        for j in range(k):
+            y += float(w[t][j]) * o[(t, j)]
+        out[i] = y
+    return out

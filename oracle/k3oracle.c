@@ -69,10 +69,10 @@ void k3o_mx_dequant(long rows, long cols, const uint8_t *codes,
                                            scales + r * (cols / 32), i);
 }
 
-/* Dot product of MX row r (length n) with an fp64 vector, ascending i.  This
- * is the pages' "multiply on the packed nibbles, never expand the matrix"
- * ([DD] "four reductions", MXFP4 paragraph; [YP] section 02, direct MXFP4
- * computation): each weight is decoded on the fly from its nibble and scale. */
+/* Dot product of MX row r (length n) with an fp64 vector, ascending i: each
+ * weight is decoded on the fly from its nibble and its block's scale, and the
+ * matrix is never expanded ([DD] "four reductions", MXFP4 note; [YP] section
+ * 02, computing on MXFP4 directly). */
 static double mx_row_dot(const uint8_t *codes, const uint8_t *scales, long n,
                          const double *v)
 {
@@ -304,6 +304,17 @@ void k3o_down(int d, int f, const double *h, const uint8_t *dc,
     #pragma omp parallel for schedule(static)
     for (long c = 0; c < d; ++c)
         o[c] = mx_row_dot(dc + c * (f / 2), ds + c * (f / 32), f, h);
+}
+
+/* Convenience: set the number of OpenMP threads (no-op without OpenMP). */
+void k3o_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
 }
 
 /* Convenience: number of threads OpenMP will use (0 when built without it). */

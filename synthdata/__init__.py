@@ -28,6 +28,7 @@ MAGIC = 0x4B334D4F
 # tensor ids inside the seed sequence
 T_ROUTER, T_GATE_CODES, T_GATE_SCALES, T_UP_CODES, T_UP_SCALES = 0, 1, 2, 3, 4
 T_DOWN_CODES, T_DOWN_SCALES, T_X, T_RANKING = 5, 6, 7, 8
+T_EDGE = 9  # the format-edge layer's extra draws (scale jitter, zero blocks)
 
 SCALE_LO, SCALE_HI = 120, 124  # E8M0 scale bytes drawn uniformly in [120, 124]
 
@@ -40,6 +41,7 @@ class LayerShape:
     E: int        # routed experts
     k: int        # experts per token
     layer: int    # seed-sequence layer id
+    fmt: str = "uniform"  # "uniform", or "edge": the format-edge construction below
 
     @property
     def expert_bytes(self) -> int:
@@ -62,6 +64,16 @@ SMALL_F512 = LayerShape("small_f512", d=512, f=512, E=12, k=3, layer=3)
 # down GEMVs, neither a multiple of 512.
 LIMIT_E1024 = LayerShape("limit_e1024", d=256, f=128, E=1024, k=32, layer=4)
 WIDE = LayerShape("wide_d8256", d=8256, f=2560, E=8, k=2, layer=5)
+# The format's edges: weight scale bytes over the whole range 0..252 (the
+# subnormal scale 2^-127 of byte 0 included) with products of ordinary size,
+# and blocks whose codes are all +0 or all -0 under any scale byte.  Column
+# block b of x is drawn at 2^-EDGE_XEXP[b], gate/up rows of d_ff block c are
+# scaled by 2^EDGE_OEXP[c] (so h by about 2^(2 EDGE_OEXP[c])), and the down
+# scales undo that; the router rows carry 2^EDGE_XEXP[b] so logits stay O(1).
+EDGE = LayerShape("edge_fmt", d=1024, f=512, E=8, k=2, layer=6, fmt="edge")
+EDGE_XEXP = np.round(np.linspace(-77, 73, EDGE.d // 32)).astype(np.int64)
+EDGE_OEXP = np.round(np.linspace(-48, 50, EDGE.f // 32)).astype(np.int64)
+EDGE_ZERO_BYTES = (0, 1, 251, 252)  # scale bytes forced onto some all-zero-code blocks
 
 
 @dataclasses.dataclass(frozen=True)
@@ -90,18 +102,30 @@ def rng(layer: int, tensor: int, index: int) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([MAGIC, layer, tensor, index]))
 
 
+def _edge_col_exp(shape: LayerShape) -> np.ndarray:
+    return np.repeat(EDGE_XEXP, 32)
+
+
 def router_weight(shape: LayerShape) -> np.ndarray:
-    """W_r fp32 [E, d], entries ~ N(0, 1/d); row e from its own stream."""
+    """W_r fp32 [E, d], entries ~ N(0, 1/d); row e from its own stream (the
+    format-edge layer: column block b times 2^EDGE_XEXP[b])."""
     w = np.empty((shape.E, shape.d), dtype=np.float32)
     sd = 1.0 / math.sqrt(shape.d)
     for e in range(shape.E):
-        w[e] = (rng(shape.layer, T_ROUTER, e).standard_normal(shape.d) * sd).astype(np.float32)
+        row = rng(shape.layer, T_ROUTER, e).standard_normal(shape.d) * sd
+        if shape.fmt == "edge":
+            row = np.ldexp(row, _edge_col_exp(shape))
+        w[e] = row.astype(np.float32)
     return w
 
 
 def token(shape: LayerShape, index: int) -> np.ndarray:
-    """One activation row, fp32 [d], entries ~ N(0, 1)."""
-    return rng(shape.layer, T_X, index).standard_normal(shape.d).astype(np.float32)
+    """One activation row, fp32 [d], entries ~ N(0, 1) (the format-edge
+    layer: column block b times 2^-EDGE_XEXP[b])."""
+    v = rng(shape.layer, T_X, index).standard_normal(shape.d)
+    if shape.fmt == "edge":
+        v = np.ldexp(v, -_edge_col_exp(shape))
+    return v.astype(np.float32)
 
 
 def tokens(shape: LayerShape, T: int, first: int = 0) -> np.ndarray:
@@ -132,7 +156,36 @@ def expert_matrix(shape: LayerShape, e: int, which: str):
     tc, ts, r, c = _MATS[which]
     rows, cols = getattr(shape, r), getattr(shape, c)
     codes = rng(shape.layer, tc, e).integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    if shape.fmt == "edge":
+        return _edge_matrix(shape, e, which, codes)
     scales = rng(shape.layer, ts, e).integers(SCALE_LO, SCALE_HI + 1, size=(rows, cols // 32), dtype=np.uint8)
+    return codes, scales
+
+
+def _edge_matrix(shape: LayerShape, e: int, which: str, codes: np.ndarray):
+    """Scale bytes of the format-edge layer (clipped to 0..252):
+    gate/up [r][b] = 127 + EDGE_XEXP[b] + EDGE_OEXP[r // 32] + U{-2..2};
+    down    [c][b] = 128 - 2 EDGE_OEXP[b] + U{-28..28}.
+    Then 5 % of the blocks get all-zero codes and 5 % all -0 codes (byte
+    0x88), and the first blocks of each kind carry the scale bytes
+    EDGE_ZERO_BYTES."""
+    r = rng(shape.layer, T_EDGE, 8 * e + ("gate", "up", "down").index(which))
+    rows, nb = codes.shape[0], codes.shape[1] // 16
+    if which == "down":
+        base = 128 - 2 * EDGE_OEXP[None, :]
+        jit = r.integers(-28, 29, size=(rows, nb))
+    else:
+        base = 127 + EDGE_XEXP[None, :] + EDGE_OEXP[np.arange(rows) // 32][:, None]
+        jit = r.integers(-2, 3, size=(rows, nb))
+    scales = np.clip(base + jit, 0, 252).astype(np.uint8)
+    kind = r.random((rows, nb))
+    blocks = codes.reshape(rows, nb, 16)
+    blocks[kind < 0.05] = 0x00
+    blocks[(kind >= 0.05) & (kind < 0.10)] = 0x88
+    for sel in (kind < 0.05, (kind >= 0.05) & (kind < 0.10)):
+        rr, bb = np.nonzero(sel)
+        n = min(len(rr), len(EDGE_ZERO_BYTES))
+        scales[rr[:n], bb[:n]] = EDGE_ZERO_BYTES[:n]
     return codes, scales
 
 

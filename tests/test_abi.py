@@ -52,6 +52,10 @@ def _ws(T, E, k, d, f, mode=0):
     ((1, 16, 2, 256, 100), -1),      # f % 32
     ((1, 2048, 2, 256, 128), -3),    # E > 1024
     ((1, 64, 33, 256, 128), -3),     # k > 32
+    ((1, 16, 2, 16384, 16384), 0),   # the widest rows the GEMVs cover
+    ((1, 16, 2, 16416, 128), -3),    # d_model > 16384: refused, never truncated
+    ((1, 16, 2, 256, 16416), -3),    # d_ff > 16384
+    ((4096, 896, 16, 16416, 2048), -3),
 ])
 def test_dims_validation(dims, rc):
     assert _ws(*dims)[0] == rc

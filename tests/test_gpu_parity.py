@@ -1,16 +1,23 @@
 """GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
 
-Small layers are compared element by element on every token; the full
-896-expert layer (d_model 7168, d_ff 2048, top-16) is compared with routing
-checked on every token and y on sampled tokens, in the launch configuration
-the benchmark times."""
+Every output is poisoned before each call (y NaN, routing -7, debug outputs
+NaN / 0xFF), so nothing the kernels skip can pass.  Small layers are compared
+element by element on every token.  The full 896-expert layer (d_model 7168,
+d_ff 2048, top-16), in the launch configuration the benchmark times: routing
+on every token; y on every token up to 64 tokens and on the 256-token skewed
+batch (fp32 activations); in MXFP4 mode x_q and h_q on every pair, and h and
+y on tokens chosen so that every active expert has a checked pair and the
+heaviest experts' last rows and pass boundaries are checked.  A format-edge
+layer puts every E8M0 byte 0..252 and all-zero / -0 code blocks through
+every path."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synthdata
-from helpers import (assert_route_equal, assert_y_close, host_expert_getter, oracle_y)
+from helpers import (assert_route_equal, assert_y_close, covering_tokens, host_expert_getter, oracle_y,
+                     oracle_y_major)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,11 +48,19 @@ def tiny():
 
 
 def _run(x, wr_dev, experts, k, bias=None, bias_mode="none", act="fp32", dbg=None, score="softmax"):
+    """k3moe_forward with every output poisoned first (y NaN, routing -7), so
+    that a row or pair the kernels never write cannot pass for a computed one."""
     xd = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     bd = None if bias is None else torch.from_numpy(bias).to(DEV)
-    y, route = k3.k3moe_forward(xd, wr_dev, experts, k, bd, bias_mode, act, dbg, score_fn=score)
+    fw = k3.Forward(xd, wr_dev, experts, k, bd, bias_mode, act, dbg, score_fn=score)
+    fw.y.fill_(float("nan"))
+    for t in fw.route.values():
+        t.fill_(-7)
+    fw()
     torch.cuda.synchronize()
-    return y.cpu().numpy(), route
+    y = fw.y.cpu().numpy()
+    assert np.isfinite(y).all(), "y has rows the kernels did not write (or non-finite values)"
+    return y, fw.route
 
 
 @pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 130, 1100])
@@ -239,38 +254,41 @@ def test_t0_is_a_noop(tiny):
 
 
 def _dbg_buffers(T, k, d, f):
+    """Debug outputs filled with sentinels: h NaN, codes and scales 0xFF (a
+    scale byte the quantiser never writes)."""
     u8 = dict(dtype=torch.uint8, device=DEV)
-    return dict(x_codes=torch.zeros((T, d // 2), **u8), x_scales=torch.zeros((T, d // 32), **u8),
-                h=torch.zeros((T * k, f), dtype=torch.float32, device=DEV),
-                h_codes=torch.zeros((T * k, f // 2), **u8), h_scales=torch.zeros((T * k, f // 32), **u8))
+    return dict(x_codes=torch.full((T, d // 2), 0xFF, **u8), x_scales=torch.full((T, d // 32), 0xFF, **u8),
+                h=torch.full((T * k, f), float("nan"), dtype=torch.float32, device=DEV),
+                h_codes=torch.full((T * k, f // 2), 0xFF, **u8), h_scales=torch.full((T * k, f // 32), 0xFF, **u8))
 
 
-def _check_mx_split(x, ref, dbg, y, get, tokens, d, f, k):
-    """Split-step parity of the MXFP4 path (see module helpers)."""
-    T = x.shape[0]
+def _check_mx_split(x, ref, dbg, y, tokens, k, get=None, shape=None):
+    """Split-step parity of the MXFP4 path: x_q bit-exact on every token, h_q
+    bit-exact on every pair (the oracle's quantiser applied to the device's
+    own fp32 h), no sentinel left in any debug output; on the given tokens, h
+    against the oracle's h from the quantised x and y against the oracle's
+    down + combine of the device's h.  Experts come from ``get`` (host
+    copies) or are regenerated from the seeds of ``shape``."""
     # 1. activation quantisation, bit-exact on every token
     xc, xs = oracle.mx_quantize(x)
     assert np.array_equal(dbg["x_codes"].cpu().numpy(), xc), "x_q codes"
     assert np.array_equal(dbg["x_scales"].cpu().numpy(), xs), "x_q scales"
     # 2. h quantisation of the device's own fp32 h, bit-exact on every pair
     h_dev = dbg["h"].cpu().numpy()
+    assert not np.isnan(h_dev).any(), "h of some pair was never written"
+    hs_dev = dbg["h_scales"].cpu().numpy()
+    assert not (hs_dev == 0xFF).any(), "h_q scales of some pair were never written"
     hc, hs = oracle.mx_quantize(h_dev)
     assert np.array_equal(dbg["h_codes"].cpu().numpy(), hc), "h_q codes"
-    assert np.array_equal(dbg["h_scales"].cpu().numpy(), hs), "h_q scales"
-    # 3. h (pre-quantisation) vs the oracle's h from the quantised x
-    h_ref = []
-    h_got = []
-    for t in tokens:
-        xt = oracle.mx_roundtrip(x[t])
-        for j, e in enumerate(ref["topk_idx"][t]):
-            ex = get(e)
-            h_ref.append(oracle.gateup(xt, ex["gate"], ex["up"]))
-            h_got.append(h_dev[t * k + j])
-    assert_y_close(np.stack(h_got), np.stack(h_ref), "h")
-    # 4. y vs the oracle's down + combine on the device's h (quantised by the oracle)
-    y_ref = oracle_y(x, ref, tokens, get, act_mode="mxfp4",
-                     h_override=lambda t: [h_dev[t * k + j] for j in range(k)])
-    assert_y_close(y[list(tokens)], y_ref, "y")
+    assert np.array_equal(hs_dev, hs), "h_q scales"
+    # 3. + 4. h and y on the chosen tokens, expert-major
+    tokens = [int(t) for t in tokens]
+    keep = {}
+    y_ref = oracle_y_major(x, ref, tokens, shape, act_mode="mxfp4",
+                           h_override=lambda t: [h_dev[t * k + j] for j in range(k)], keep=keep, get=get)
+    pairs = [(t, j) for t in tokens for j in range(k)]
+    assert_y_close(np.stack([h_dev[t * k + j] for t, j in pairs]), np.stack([keep["h"][p] for p in pairs]), "h")
+    assert_y_close(y[tokens], y_ref, "y")
 
 
 @pytest.mark.parametrize("T", [1, 37, 300, 1100])
@@ -283,7 +301,7 @@ def test_tiny_mx_split_step(tiny, T):
     ref = oracle.route(x, tiny["wr"], sh.k)
     assert_route_equal(route, ref)
     toks = range(T) if T <= 300 else range(0, T, 7)
-    _check_mx_split(x, ref, dbg, y, tiny["get"], toks, sh.d, sh.f, sh.k)
+    _check_mx_split(x, ref, dbg, y, toks, sh.k, get=tiny["get"])
 
 
 # ------------------------------------------------ small d_ff % 512 layers ---
@@ -362,7 +380,7 @@ def test_small_mx_split_step(small, T):
     ref = oracle.route(x, small["wr"], sh.k)
     assert_route_equal(route, ref)
     toks = range(T) if T <= 300 else range(0, T, 5)
-    _check_mx_split(x, ref, dbg, y, small["get"], toks, sh.d, sh.f, sh.k)
+    _check_mx_split(x, ref, dbg, y, toks, sh.k, get=small["get"])
 
 
 # ------------------------------------------------------ contract limits ---
@@ -408,7 +426,46 @@ def test_wide_mx_split_step(T):
     y, route = _run(x, L["wr_dev"], L["dev"], sh.k, act="mxfp4", dbg=dbg)
     ref = oracle.route(x, L["wr"], sh.k)
     assert_route_equal(route, ref)
-    _check_mx_split(x, ref, dbg, y, L["get"], range(T), sh.d, sh.f, sh.k)
+    _check_mx_split(x, ref, dbg, y, range(T), sh.k, get=L["get"])
+
+
+# ---------------------------------------------------------- format edges ---
+@pytest.fixture(scope="module")
+def edge():
+    sh = synthdata.EDGE
+    host = synthdata.all_experts_host(sh)
+    wr = synthdata.router_weight(sh)
+    return dict(shape=sh, host=host, dev=_to_dev_experts(host), wr=wr,
+                wr_dev=torch.from_numpy(wr).to(DEV), get=host_expert_getter(sh, host))
+
+
+@pytest.mark.parametrize("T", [1, 3, 70, 300])
+def test_edge_format_fp32(edge, T):
+    """Weights whose scale bytes take every value 0..252 (byte 0: the
+    subnormal scale 2^-127), with products of ordinary size, and blocks of
+    all-zero and all -0 codes under any scale byte, in gate, up and down:
+    T = 1, 3 the pair path (down on the matrix cores), 70 the grouped GEMVs,
+    300 also the int8 router (its bound is wide here: every token falls back
+    to the fp64 recompute)."""
+    sh = edge["shape"]
+    _log(f"edge fp32 T={T}")
+    x = synthdata.tokens(sh, T, first=40 + T)
+    y, route = _run(x, edge["wr_dev"], edge["dev"], sh.k)
+    ref = oracle.route(x, edge["wr"], sh.k)
+    assert_route_equal(route, ref)
+    assert_y_close(y, oracle_y(x, ref, range(T), edge["get"]))
+
+
+@pytest.mark.parametrize("T", [1, 70, 300])
+def test_edge_format_mx_split_step(edge, T):
+    sh = edge["shape"]
+    _log(f"edge mx T={T}")
+    x = synthdata.tokens(sh, T, first=90 + T)
+    dbg = _dbg_buffers(T, sh.k, sh.d, sh.f)
+    y, route = _run(x, edge["wr_dev"], edge["dev"], sh.k, act="mxfp4", dbg=dbg)
+    ref = oracle.route(x, edge["wr"], sh.k)
+    assert_route_equal(route, ref)
+    _check_mx_split(x, ref, dbg, y, range(T), sh.k, get=edge["get"])
 
 
 # ----------------------------------------------------------- full layer ---
@@ -474,21 +531,25 @@ def test_k3_small_batch_t8(k3layer):
     y, route = _run(x, k3layer["wr_dev"], k3layer["dev"], sh.k)
     ref = oracle.route(x, k3layer["wr"], sh.k)
     assert_route_equal(route, ref)
-    assert_y_close(y, oracle_y(x, ref, range(8), k3layer["get"]))
+    assert_y_close(y, oracle_y_major(x, ref, range(8), sh))
 
 
 def test_k3_batch_t64(k3layer):
+    """The 64-token batch (grouped GEMVs): y on every token."""
     sh = k3layer["shape"]
     x = synthdata.tokens(sh, 64)
     y, route = _run(x, k3layer["wr_dev"], k3layer["dev"], sh.k)
     ref = oracle.route(x, k3layer["wr"], sh.k)
     assert_route_equal(route, ref)
-    toks = [0, 1, 17, 31, 32, 50, 62, 63]
-    _log("k3 T=64 oracle rows")
-    assert_y_close(y[toks], oracle_y(x, ref, toks, k3layer["get"]))
+    _log(f"k3 T=64: oracle on all 64 tokens ({int((ref['counts'] > 0).sum())} experts)")
+    assert_y_close(y, oracle_y_major(x, ref, range(64), sh))
 
 
 def test_k3_prefill_t4096_mx(k3layer):
+    """4096-token prefill, MXFP4 activations: routing on every token, x_q and
+    h_q on every pair, h and y on >= 128 tokens that give every active expert
+    a checked pair and check the last rows of the 16 heaviest experts and
+    their row 96 (past the first 96-token pass)."""
     sh = k3layer["shape"]
     T = 4096
     x = synthdata.tokens(sh, T)
@@ -497,10 +558,15 @@ def test_k3_prefill_t4096_mx(k3layer):
     _log("k3 T=4096 oracle routing")
     ref = oracle.route(x, k3layer["wr"], sh.k)
     assert_route_equal(route, ref)
-    _check_mx_split(x, ref, dbg, y, k3layer["get"], [0, 1, 2047, 4095], sh.d, sh.f, sh.k)
+    toks = covering_tokens(ref, 128, seed=4096)
+    _log(f"k3 T=4096 oracle h and y on {len(toks)} tokens")
+    _check_mx_split(x, ref, dbg, y, toks, sh.k, shape=sh)
 
 
 def test_k3_skew_t256(k3layer):
+    """Zipf-skewed 256-token batch (bias in the logits): MXFP4 split-step on
+    >= 96 tokens covering every active expert and the heavy experts' last
+    rows; fp32 activations end to end on every token."""
     sh = k3layer["shape"]
     T = 256
     x = synthdata.tokens(sh, T)
@@ -511,9 +577,30 @@ def test_k3_skew_t256(k3layer):
     y, route = _run(x, k3layer["wr_dev"], k3layer["dev"], sh.k, bias, "logits", act="mxfp4", dbg=dbg)
     assert_route_equal(route, ref)
     counts = ref["counts"]
-    _log(f"k3 skew: {int((counts > 0).sum())} active experts, max {counts.max()} tokens/expert")
-    _check_mx_split(x, ref, dbg, y, k3layer["get"], [0, 100, 255], sh.d, sh.f, sh.k)
-    # fp32 path end to end
+    toks = covering_tokens(ref, 96, seed=256)
+    _log(f"k3 skew: {int((counts > 0).sum())} active experts, max {counts.max()} tokens/expert; "
+         f"mx on {len(toks)} tokens")
+    _check_mx_split(x, ref, dbg, y, toks, sh.k, shape=sh)
+    # fp32 path end to end, every token
     y32, route32 = _run(x, k3layer["wr_dev"], k3layer["dev"], sh.k, bias, "logits")
     assert_route_equal(route32, ref)
-    assert_y_close(y32[[0, 128, 255]], oracle_y(x, ref, [0, 128, 255], k3layer["get"]))
+    _log("k3 skew fp32: oracle on all 256 tokens")
+    assert_y_close(y32, oracle_y_major(x, ref, range(T), sh))
+
+
+def test_k3_prefill_t32768_mx_sampled(k3layer):
+    """The compute-bound prefill shape (32,768 tokens, ~585 per expert):
+    routing on every token, x_q and h_q on every pair, h and y on tokens that
+    cover every active expert, the heaviest experts' last rows and the rows
+    where 128-token passes begin."""
+    sh = k3layer["shape"]
+    T = 32768
+    x = synthdata.tokens(sh, T)
+    dbg = _dbg_buffers(T, sh.k, sh.d, sh.f)
+    y, route = _run(x, k3layer["wr_dev"], k3layer["dev"], sh.k, act="mxfp4", dbg=dbg)
+    _log("k3 T=32768 oracle routing")
+    ref = oracle.route(x, k3layer["wr"], sh.k)
+    assert_route_equal(route, ref)
+    toks = covering_tokens(ref, 80, seed=32768, n_heavy=8, pass_rows=(96, 128, 256, 384, 512))
+    _log(f"k3 T=32768 oracle h and y on {len(toks)} tokens")
+    _check_mx_split(x, ref, dbg, y, toks, sh.k, shape=sh)

@@ -179,3 +179,60 @@ def test_mx_mode_uses_quantised_activations():
     assert np.array_equal(y, ref)
     y32 = oracle.token_forward(x, [1, 2], [0.6, 0.4], get)
     assert not np.allclose(y, y32, rtol=1e-3)   # a different function, as expected
+
+
+@pytest.mark.parametrize("act_mode", ["fp32", "mxfp4"])
+@pytest.mark.parametrize("override", [False, True])
+def test_layer_forward_is_token_forward(act_mode, override):
+    """The expert-major evaluation (each expert visited once for all of its
+    pairs) forms every token's sum with the same fp64 operations in the same
+    order as token_forward, so the two agree bit for bit."""
+    sh = synthdata.TINY
+    host = synthdata.all_experts_host(sh)
+    get = lambda e: {w: (host[w][0][e], host[w][1][e]) for w in host}  # noqa: E731
+    x = synthdata.tokens(sh, 40, first=123)
+    r = oracle.route(x, synthdata.router_weight(sh), sh.k)
+    rng = np.random.default_rng(5)
+    hs = rng.standard_normal((40, sh.k, sh.f)).astype(np.float32)
+    hov = (lambda t: list(hs[t])) if override else None
+    toks = [39, 0, 7, 8, 21]
+    seen = []
+
+    def get_logged(e):
+        seen.append(e)
+        return get(e)
+
+    keep = {}
+    got = oracle.layer_forward(x, r, toks, get_logged, act_mode=act_mode, h_override=hov, keep=keep)
+    assert seen == sorted(set(seen)), "experts are fetched once each, ascending"
+    for i, t in enumerate(toks):
+        kt = {}
+        ref = oracle.token_forward(x[t], r["topk_idx"][t], r["topk_w"][t], get, act_mode=act_mode,
+                                   h_override=None if hov is None else hov(t), keep=kt)
+        assert np.array_equal(got[i], ref)
+        for j in range(sh.k):
+            assert np.array_equal(keep["h"][(t, j)], kt["h"][j])
+
+
+def test_ffn_vs_dense_matmul_format_edges():
+    """The format-edge layer (scale bytes over 0..252, the subnormal 2^-127
+    included, and all-zero / all -0 code blocks under any scale byte): the
+    oracle's expert FFN still equals the dense fp64 product of the bit-decoded
+    weights, and every byte value and both zero-block kinds are present."""
+    sh = synthdata.EDGE
+    x = synthdata.tokens(sh, 3, first=11).astype(np.float64)
+    for e in (0, 5):
+        ex = synthdata.expert(sh, e)
+        for w in ("gate", "up", "down"):
+            c, s = ex[w]
+            assert set(np.unique(s)) == set(range(253)), w
+            blocks = c.reshape(c.shape[0], -1, 16)
+            zero = (blocks == 0).all(-1)
+            negz = (blocks == 0x88).all(-1)
+            for b in synthdata.EDGE_ZERO_BYTES:
+                assert (s[zero] == b).any() and (s[negz] == b).any(), (w, b)
+        for t in range(3):
+            got = oracle.expert_ffn(x[t], ex)
+            ref = _dense_ffn(x[t], ex)
+            assert np.all(np.isfinite(ref))
+            assert np.linalg.norm(got - ref) <= 1e-12 * np.linalg.norm(ref)
