@@ -185,6 +185,30 @@ int k3moe_forward(const k3moe_dims *dims, const float *x, const float *w_router,
                   int32_t *row_of_pair, float *y, const k3moe_debug *dbg,
                   void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* k3moe_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The scratch it needs comes from a
+ * fixed array of K3MOE_NOALLOC_SCRATCH_BYTES in the library's own device
+ * memory, one per device, reserved when the library's code is loaded on that
+ * device and held until the process ends; its address is looked up once per
+ * device on the first call.  Dimensions whose workspace
+ * (k3moe_workspace_size) exceeds that size are refused with
+ * K3MOE_EWORKSPACE before any HIP call: at the 896-expert layer (d_model
+ * 7168, d_ff 2048, top-16) that admits single-token decode and batches of up
+ * to about 90 tokens.  This call allocates nothing and frees nothing.  All
+ * calls on one device share its array and leave their contents in it (the
+ * kernels write every scratch byte they read before reading it): calls that
+ * overlap in time on one device -- on different streams or threads -- race
+ * and give undefined results; calls ordered on one stream do not.  Other
+ * arguments, outputs and errors as k3moe_forward. */
+#define K3MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int k3moe_forward_noalloc(const k3moe_dims *dims, const float *x, const float *w_router,
+                          const float *bias, int bias_mode, int score_fn,
+                          const k3moe_experts *experts, int act_mode, int32_t *topk_idx,
+                          float *topk_w, int32_t *counts, int32_t *offsets,
+                          int32_t *perm_pair, int32_t *row_of_pair, float *y,
+                          const k3moe_debug *dbg, hipStream_t stream);
+
 /* Human-readable text of a status code (static storage). */
 const char *k3moe_status_string(int status);
 

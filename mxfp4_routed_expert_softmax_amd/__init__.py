@@ -22,8 +22,9 @@ K3MOE_BIAS_NONE, K3MOE_BIAS_LOGITS, K3MOE_BIAS_SELECT_ONLY = 0, 1, 2
 K3MOE_ACT_FP32, K3MOE_ACT_MXFP4 = 0, 1
 K3MOE_SCORE_SOFTMAX, K3MOE_SCORE_SIGMOID = 0, 1
 
-EXPORTS = ("k3moe_workspace_size", "k3moe_route", "k3moe_ffn", "k3moe_forward",
+EXPORTS = ("k3moe_workspace_size", "k3moe_route", "k3moe_ffn", "k3moe_forward", "k3moe_forward_noalloc",
            "k3moe_status_string", "k3moe_last_hip_error")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # K3MOE_NOALLOC_SCRATCH_BYTES
 
 _BIAS = {"none": K3MOE_BIAS_NONE, "logits": K3MOE_BIAS_LOGITS, "select_only": K3MOE_BIAS_SELECT_ONLY}
 _ACT = {"fp32": K3MOE_ACT_FP32, "mxfp4": K3MOE_ACT_MXFP4}
@@ -74,10 +75,12 @@ def _lib():
                                 ctypes.POINTER(Debug), P, SZ, P]
         L.k3moe_forward.argtypes = [DP, P, P, P, I, I, ctypes.POINTER(Experts), I, P, P, P, P, P, P, P,
                                     ctypes.POINTER(Debug), P, SZ, P]
+        L.k3moe_forward_noalloc.argtypes = [DP, P, P, P, I, I, ctypes.POINTER(Experts), I, P, P, P, P, P, P, P,
+                                            ctypes.POINTER(Debug), P]
         L.k3moe_status_string.argtypes = [I]
         L.k3moe_status_string.restype = ctypes.c_char_p
         L.k3moe_last_hip_error.argtypes = []
-        for name in ("k3moe_workspace_size", "k3moe_route", "k3moe_ffn", "k3moe_forward",
+        for name in ("k3moe_workspace_size", "k3moe_route", "k3moe_ffn", "k3moe_forward", "k3moe_forward_noalloc",
                      "k3moe_last_hip_error"):
             getattr(L, name).restype = I
         _L = L
@@ -257,3 +260,33 @@ def k3moe_forward(x, w_router, experts, k, bias=None, bias_mode="none", act_mode
     fw = Forward(x, w_router, experts, k, bias, bias_mode, act_mode, dbg, stream, score_fn)
     y = fw()
     return y, fw.route
+
+
+def k3moe_forward_noalloc(x, w_router, experts, k, bias=None, bias_mode="none", act_mode="fp32", dbg=None,
+                          stream=None, score_fn="softmax", out=None):
+    """Route + expert FFN + combine through k3moe_forward_noalloc: no
+    workspace; the library's fixed per-device scratch is used instead.
+    ``out`` optionally gives (y, routing dict) to write into.  Returns (y,
+    routing dict)."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    f = experts["gate"][0].shape[1]
+    _need(x, torch.float32, (T, d), "x")
+    _need(w_router, torch.float32, (E, d), "w_router")
+    if bias is not None:
+        _need(bias, torch.float32, (E,), "bias")
+    if out is None:
+        y = torch.empty((T, d), dtype=torch.float32, device=x.device)
+        route = alloc_route(T, E, k, x.device)
+    else:
+        y, route = out
+        _need(y, torch.float32, (T, d), "y")
+    ex = make_experts(experts, E, d, f)
+    dims = Dims(T, E, k, d, f)
+    dstruct = _debug_struct(dbg)
+    r = [_ptr(route[n]) for n in ("topk_idx", "topk_w", "counts", "offsets", "perm_pair", "row_of_pair")]
+    rc = _lib().k3moe_forward_noalloc(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(bias), _BIAS[bias_mode],
+                                      _SCORE[score_fn], ctypes.byref(ex), _ACT[act_mode], *r, _ptr(y),
+                                      ctypes.byref(dstruct) if dstruct is not None else None, _stream(stream))
+    _check(rc, "k3moe_forward_noalloc")
+    return y, route

@@ -7,6 +7,7 @@
 // correctness and reproducibility).  All checks run before the first HIP call.
 #include <string.h>
 #include <atomic>
+#include <mutex>
 #include "k3moe.h"
 #include "kernels.h"
 
@@ -368,12 +369,76 @@ int k3moe_forward(const k3moe_dims* dims, const float* x, const float* w_router,
     return rc ? rc : finish_launches();
 }
 
+// Scratch of k3moe_forward_noalloc: one array per device in the library's
+// own device memory.  Host code never uses the array's name as an address
+// (on the host it names a stand-in, not device memory): the device address
+// is looked up once per device with hipGetSymbolAddress and kept here.
+static __device__ __align__(256) uint8_t scratch[K3MOE_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+static int g_scratch_err[64];  // hipError_t of a failed lookup, kept so a retry reports it
+
+static int scratch_ptr(void** out)
+{
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return K3MOE_EHIP;
+    }
+    if (dev < 0 || dev >= 64) return K3MOE_ENOTSUP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev] && !g_scratch_err[dev]) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with device dev current
+        if (err != hipSuccess || !p)
+            g_scratch_err[dev] = err != hipSuccess ? (int)err : (int)hipErrorInvalidSymbol;
+        else
+            g_scratch_ptr[dev] = p;
+    }
+    if (g_scratch_err[dev]) {
+        g_last_hip_error = g_scratch_err[dev];
+        return K3MOE_EHIP;
+    }
+    *out = g_scratch_ptr[dev];
+    return K3MOE_OK;
+}
+
+int k3moe_forward_noalloc(const k3moe_dims* dims, const float* x, const float* w_router, const float* bias,
+                          int bias_mode, int score_fn, const k3moe_experts* experts, int act_mode,
+                          int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                          int32_t* perm_pair, int32_t* row_of_pair, float* y, const k3moe_debug* dbg,
+                          hipStream_t stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if ((rc = check_mode_act(act_mode))) return rc;
+    if (dims->T == 0) return K3MOE_OK;
+    const size_t need = ws_layout(dims->T, dims->E, dims->k, dims->d_model, dims->d_ff, act_mode).total;
+    if (need > K3MOE_NOALLOC_SCRATCH_BYTES) return K3MOE_EWORKSPACE;
+    // the remaining checks are k3moe_forward's, on a stand-in workspace
+    // address (aligned, never dereferenced) before the first HIP call
+    void* const probe = reinterpret_cast<void*>((uintptr_t)256);
+    rc = validate_route(dims, x, w_router, bias, bias_mode, score_fn, topk_idx, topk_w, counts, offsets,
+                        perm_pair, row_of_pair, probe, K3MOE_NOALLOC_SCRATCH_BYTES, act_mode);
+    if (rc) return rc;
+    rc = validate_ffn(dims, x, experts, topk_idx, topk_w, counts, offsets, perm_pair, row_of_pair, act_mode, y,
+                      probe, K3MOE_NOALLOC_SCRATCH_BYTES);
+    if (rc) return rc;
+    if ((rc = check_device())) return rc;
+    void* ws = nullptr;
+    if ((rc = scratch_ptr(&ws))) return rc;
+    return k3moe_forward(dims, x, w_router, bias, bias_mode, score_fn, experts, act_mode, topk_idx, topk_w, counts,
+                         offsets, perm_pair, row_of_pair, y, dbg, ws, K3MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 const char* k3moe_status_string(int status)
 {
     switch (status) {
         case K3MOE_OK: return "ok";
         case K3MOE_EINVAL: return "invalid argument (dimension, null or misaligned pointer)";
-        case K3MOE_EWORKSPACE: return "workspace missing or too small";
+        case K3MOE_EWORKSPACE: return "workspace missing or too small (k3moe_forward_noalloc: the dimensions need more than its fixed scratch)";
         case K3MOE_ENOTSUP: return "not supported (mode, E > 1024, k > 32, d_model or d_ff > 16384, or device is not gfx950)";
         case K3MOE_EHIP: return "HIP error (see k3moe_last_hip_error)";
         default: return "unknown status";

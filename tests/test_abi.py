@@ -140,3 +140,36 @@ def test_binding_refuses_wrong_tensors():
     x = torch.zeros((2, 256), dtype=torch.float64)
     with pytest.raises(ValueError):
         k3._need(x, torch.float32, (2, 256), "x")
+
+
+def test_noalloc_scratch_limit_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define K3MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == k3.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_refuses_dimensions_beyond_its_scratch_without_touching_the_gpu():
+    lib = k3.lib()
+    fake = ctypes.c_void_p(0x10000)
+    mx = k3.MX(0x10000, 0x10000)
+    ex = k3.Experts(mx, mx, mx)
+    # x, w_router, bias, bias_mode, score_fn, experts, act, 6 routing outputs, y, dbg, stream
+    args = [fake, fake, None, 0, 0, ctypes.byref(ex), 0] + [fake] * 6 + [fake, None, None]
+    for T, act in ((4096, 0), (4096, 1), (200, 0)):
+        dims = k3.Dims(T, 896, 16, 7168, 2048)
+        a = list(args)
+        a[6] = act
+        assert _ws(T, 896, 16, 7168, 2048, act)[1] > k3.NOALLOC_SCRATCH_BYTES
+        assert lib.k3moe_forward_noalloc(ctypes.byref(dims), *a) == k3.K3MOE_EWORKSPACE
+    # the usual argument checks come first, as in k3moe_forward
+    dims = k3.Dims(1, 896, 16, 7168, 2048)
+    a = list(args)
+    a[0] = None
+    assert lib.k3moe_forward_noalloc(ctypes.byref(dims), *a) == k3.K3MOE_EINVAL
+    a = list(args)
+    a[6] = 9
+    assert lib.k3moe_forward_noalloc(ctypes.byref(dims), *a) == k3.K3MOE_ENOTSUP
+    z = k3.Dims(0, 896, 16, 7168, 2048)
+    assert lib.k3moe_forward_noalloc(ctypes.byref(z), *([None] * 3 + [0, 0, None, 0] + [None] * 9)) == 0
+    # single-token decode fits
+    assert _ws(1, 896, 16, 7168, 2048, 0)[1] <= k3.NOALLOC_SCRATCH_BYTES
