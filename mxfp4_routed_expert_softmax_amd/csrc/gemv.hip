@@ -229,7 +229,7 @@ void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h, uint8_t* __restrict__ 
                 const uint32_t row = (uint32_t)(pb + (i % HALF));
 #pragma unroll
                 for (int b = 0; b < BPL; ++b) {
-                    q[i][b] = ld_codes(i < HALF ? rg : ru, coff[b], row * (uint32_t)crow);
+                    q[i][b] = ld_stream(i < HALF ? rg : ru, coff[b], row * (uint32_t)crow);
                     sb[i][b] = ld_scale(i < HALF ? rgs : rus, soffl[b], row * (uint32_t)srow);
                 }
             }
@@ -285,6 +285,128 @@ void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h, uint8_t* __restrict__ 
     }
 }
 
+// Grouped gate/up, one token per pass: the weights of a batch are loaded once
+// and applied to every token of the expert (up to kGuTokChunk per weight
+// pass), each token's activation block re-read from L2 per batch, so an
+// expert with n tokens streams its rows from HBM once instead of n times.
+// Per token the sums are formed exactly as in gateup_gemv_kernel<1, BPL,
+// false> (same per-lane order, same reductions): identical results.  Used
+// for d <= 8192 (BPL = 1); two blocks per lane would not fit the registers.
+constexpr int kGuTokChunk = 8;
+
+template <int BPL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void gateup_gemv_tokens_kernel(FfnArgs a, float* __restrict__ h)
+{
+    constexpr int R = 16, HALF = R / 2;
+    __shared__ float part[kGuTokChunk][4][kGuRows * 2];  // [token][wave][gate rows | up rows]
+    int e, r_beg, n_e;
+    if (!slot_expert(a, blockIdx.y, e, r_beg, n_e)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r0 = blockIdx.x * kGuRows;
+    const int d = a.d, nb = d >> 5;
+    const size_t crow = (size_t)(d >> 1), srow = (size_t)nb;
+    const size_t wrow0 = (size_t)e * a.f + r0;
+    const int npairs = min(kGuRows, a.f - r0);  // multiple of 8 (f % 32 == 0)
+    const __amdgpu_buffer_rsrc_t rg = weight_rsrc(a.gc + wrow0 * crow);
+    const __amdgpu_buffer_rsrc_t ru = weight_rsrc(a.uc + wrow0 * crow);
+    const __amdgpu_buffer_rsrc_t rgs = weight_rsrc(a.gs + wrow0 * srow);
+    const __amdgpu_buffer_rsrc_t rus = weight_rsrc(a.us + wrow0 * srow);
+    uint32_t coff[BPL], soffl[BPL];
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+        const int blk = tid + 256 * b;
+        coff[b] = blk < nb ? (uint32_t)blk * 16u : kOff;
+        soffl[b] = blk < nb ? (uint32_t)blk : kOff;
+    }
+    for (int t0 = 0; t0 < n_e; t0 += kGuTokChunk) {
+        const int nt = min(kGuTokChunk, n_e - t0);
+        for (int pb = 0; pb < npairs; pb += HALF) {
+            uint4 q[R][BPL];
+            uint32_t sb[R][BPL];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const uint32_t row = (uint32_t)(pb + (i % HALF));
+#pragma unroll
+                for (int b = 0; b < BPL; ++b) {
+                    q[i][b] = ld_stream(i < HALF ? rg : ru, coff[b], row * (uint32_t)crow);
+                    sb[i][b] = ld_scale(i < HALF ? rgs : rus, soffl[b], row * (uint32_t)srow);
+                }
+            }
+            float sc[R][BPL];
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+                for (int b = 0; b < BPL; ++b) sc[i][b] = e8m0_f32(sb[i][b]);
+            for (int tt = 0; tt < nt; ++tt) {
+                const int tok = a.perm_pair[r_beg + t0 + tt] / a.k;
+                const float* xrow = a.x + (size_t)tok * d;
+#pragma unroll
+                for (int i = 0; i < R; ++i)
+#pragma unroll
+                    for (int b = 0; b < BPL; ++b) opaque(q[i][b]);  // decode per token, not hoisted out of the loop
+                float acc[16];
+#pragma unroll
+                for (int i = 0; i < R; ++i) acc[i] = 0.f;
+                // per row the products are added in the order of dot32_multi
+                // (block b, then code word k, then the 8 values of the word);
+                // only the loop over rows moved inside, so 8 activation
+                // values are live at a time
+#pragma unroll
+                for (int b = 0; b < BPL; ++b) {
+                    const int blk = tid + 256 * b;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        float x8[8];
+                        if (blk < nb) {
+                            const float4* xp = reinterpret_cast<const float4*>(xrow + (size_t)blk * 32 + 8 * k);
+                            const float4 u0 = xp[0], u1 = xp[1];
+                            x8[0] = u0.x; x8[1] = u0.y; x8[2] = u0.z; x8[3] = u0.w;
+                            x8[4] = u1.x; x8[5] = u1.y; x8[6] = u1.z; x8[7] = u1.w;
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) x8[j] = 0.f;
+                        }
+#pragma unroll
+                        for (int i = 0; i < R; ++i) {
+                            const uint32_t w = k == 0 ? q[i][b].x : k == 1 ? q[i][b].y : k == 2 ? q[i][b].z : q[i][b].w;
+                            const f32x2 p0 = fp4x2_scaled<0>(w, sc[i][b]);
+                            const f32x2 p1 = fp4x2_scaled<1>(w, sc[i][b]);
+                            const f32x2 p2 = fp4x2_scaled<2>(w, sc[i][b]);
+                            const f32x2 p3 = fp4x2_scaled<3>(w, sc[i][b]);
+                            float t = acc[i];
+                            t = __builtin_fmaf(p0.x, x8[0], t);
+                            t = __builtin_fmaf(p0.y, x8[1], t);
+                            t = __builtin_fmaf(p1.x, x8[2], t);
+                            t = __builtin_fmaf(p1.y, x8[3], t);
+                            t = __builtin_fmaf(p2.x, x8[4], t);
+                            t = __builtin_fmaf(p2.y, x8[5], t);
+                            t = __builtin_fmaf(p3.x, x8[6], t);
+                            t = __builtin_fmaf(p3.y, x8[7], t);
+                            acc[i] = t;
+                        }
+                    }
+                }
+                const float v = wave_transpose_sum16(acc);
+                if (lane < 16) part[tt][wave][lane < HALF ? pb + lane : kGuRows + pb + lane - HALF] = v;
+            }
+        }
+        __syncthreads();
+        // fixed-order cross-wave sum; thread (tt, r) finishes row r of token tt
+        for (int i = tid; i < nt * npairs; i += 256) {
+            const int tt = i / npairs, r = i - tt * npairs;
+            float g = 0.f, u = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                g += part[tt][w][r];
+                u += part[tt][w][kGuRows + r];
+            }
+            h[(size_t)(r_beg + t0 + tt) * a.f + r0 + r] = silu_f32(g) * u;
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------------------
 // down.  Block = 4 waves; NK waves split the f axis (one block per lane, BPL
 // per lane beyond 64*NK blocks), 4/NK teams of waves take different rows.
@@ -330,7 +452,7 @@ void down_gemv_kernel(FfnArgs a, const float* __restrict__ hbuf,
             uint32_t sb[R];
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                q[i][b] = ld_codes(rd, coff[b], (uint32_t)(rb + i) * (uint32_t)crow);
+                q[i][b] = ld_stream(rd, coff[b], (uint32_t)(rb + i) * (uint32_t)crow);
                 sb[i] = ld_scale(rds, soffl[b], (uint32_t)(rb + i) * (uint32_t)srow);
             }
 #pragma unroll
@@ -455,7 +577,7 @@ __global__ __launch_bounds__(64 * kGatherWaves) void down_gather_kernel(FfnArgs 
 #pragma unroll
                 for (int b = 0; b < BPL; ++b) {
                     if (row < RW) {
-                        q[i][b] = ld_codes(rd, coff[b], (uint32_t)row * (uint32_t)crow);
+                        q[i][b] = ld_stream(rd, coff[b], (uint32_t)row * (uint32_t)crow);
                         sb[i][b] = ld_scale(rds, soffl[b], (uint32_t)row * (uint32_t)srow);
                     } else {
                         q[i][b] = make_uint4(0u, 0u, 0u, 0u);
@@ -554,11 +676,15 @@ void launch_gateup_gemv_slices(const FfnArgs& a, uint8_t* hs_codes, uint8_t* hs_
 
 void launch_gateup_gemv(const FfnArgs& a, float* h, hipStream_t s)
 {
-    if (use_pair_path(a))
+    if (use_pair_path(a)) {
         gateup_dispatch<1, true>(a, h, s);
-    else if (tokens_per_pass(a) == 1)
+    } else if (tokens_per_pass(a) == 1 && a.d / 32 <= 256) {
+        // (two blocks per lane do not fit its registers: wider d keeps the token-outer form)
+        const dim3 grid((a.f + kGuRows - 1) / kGuRows, a.nslots);
+        gateup_gemv_tokens_kernel<1><<<grid, dim3(256), 0, s>>>(a, h);
+    } else if (tokens_per_pass(a) == 1) {
         gateup_dispatch<1, false>(a, h, s);
-    else
+    } else
         gateup_dispatch<2, false>(a, h, s);
 }
 
