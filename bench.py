@@ -55,8 +55,9 @@ def parse():
                     help="timed steps of the 4096-token MXFP4 prefill reported under 'prefill' "
                          "(0 disables it; only with the headline decode workload)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
-                    help="after timing, run a plain device copy of this many MiB three times "
-                         "(reference kernel for hardware byte counters; not part of the step)")
+                    help="after timing, copy this many MiB three times with the runtime's copy and three "
+                         "times with an elementwise kernel (reference kernels for hardware byte counters; "
+                         "not part of the step)")
     return ap.parse_args()
 
 
@@ -122,7 +123,9 @@ def main():
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            dst.copy_(src)                 # the runtime's blit kernel
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)   # an elementwise kernel: one 16-byte load and store per lane step
         torch.cuda.synchronize()
         del src, dst
 

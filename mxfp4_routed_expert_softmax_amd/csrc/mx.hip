@@ -1,8 +1,9 @@
 // mx.hip -- MXFP4-activation expert FFN for gfx950: activation quantiser,
-// grouped gate/up GEMM with fused SwiGLU + h quantiser, grouped down GEMM with
-// fused gate-weighted scatter-add combine.  Both GEMMs run on the CDNA4
-// scaled matrix cores (V_MFMA_SCALE_F32_16X16X128_F8F6F4, FP4 x FP4 with
-// E8M0 block scales, fp32 accumulate).
+// grouped gate/up GEMM with fused SwiGLU + h quantiser, grouped down GEMM
+// writing one fp32 output row per token-expert pair (the gate-weighted
+// combine of those rows is combine_kernel, a deterministic gather).  Both
+// GEMMs run on the CDNA4 scaled matrix cores (V_MFMA_SCALE_F32_16X16X128_F8F6F4,
+// FP4 x FP4 with E8M0 block scales, fp32 accumulate).
 //
 // Weights stay in the pages' format: 4-bit E2M1 codes with one E8M0 scale per
 // 32 values along the reduction axis (fiv.co.kr "kimi-k3-in-c deep dive",
