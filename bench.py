@@ -54,6 +54,11 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=10,
                     help="timed steps of the 4096-token MXFP4 prefill reported under 'prefill' "
                          "(0 disables it; only with the headline decode workload)")
+    ap.add_argument("--cache-slots", type=int, default=256,
+                    help="after the headline decode run, the same decode through the HBM expert cache "
+                         "(k3moe_forward_cached) with this many expert slots, every expert in pinned host "
+                         "memory; 0 skips it")
+    ap.add_argument("--cache-steps", type=int, default=200, help="timed steps of the cached decode")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, copy this many MiB three times with the runtime's copy and three "
                          "times with an elementwise kernel (reference kernels for hardware byte counters; "
@@ -97,6 +102,11 @@ def main():
                    "tokens_per_s": round(pm["tokens_per_s"], 1), "roofline": pm["roofline"],
                    "active_experts_last_step": pm["n_active"]}
         del pm
+
+    cache = None
+    if args.cache_slots > 0 and wl.name == "k3_decode_t1" and not args.graph:
+        log(f"cache block: {args.cache_slots} slots")
+        cache = measure_cache(k3, synthdata, torch, wl, experts, wr, xs, args.cache_slots, args.cache_steps)
 
     flushed = None
     if args.flush_mib > 0:
@@ -156,6 +166,8 @@ def main():
     }
     if prefill is not None:
         out["prefill"] = prefill
+    if cache is not None:
+        out["cache"] = cache
     if flushed is not None:
         out["flushed"] = flushed
     print(json.dumps(out), flush=True)
@@ -255,6 +267,67 @@ def measure(k3, synthdata, torch, dev, wl, experts, wr, steps, warmup, use_graph
     return dict(fw=fw, xs=xs, nbatch=nbatch, stream=stream, ms_per_step=ms_per_step,
                 tokens_per_s=tokens_per_s, roofline=roofline, n_active=n_active, bias_mode=bias_mode,
                 graph=graph)
+
+
+def measure_cache(k3, synthdata, torch, wl, experts, wr, xs, n_slots, steps):
+    """Single-token decode through k3moe_forward_cached: every expert in
+    pinned host memory, n_slots of them in HBM under the step-batched LRU.
+    The cache is warmed with n_slots // k steps of other tokens, then `steps`
+    fresh tokens are timed end to end (routing, policy, copies of the missed
+    experts over the host link, expert FFN).  Hit rate from the device
+    counters, checked against the oracle's LRU replay of the same selections,
+    with Belady's optimum on that trace for comparison."""
+    from oracle import cache as oc
+    sh = wl.shape
+    t0 = time.time()
+    host = {}
+    for w, (c, sc) in experts.items():
+        hc = torch.empty(c.shape, dtype=torch.uint8, pin_memory=True)
+        hs = torch.empty(sc.shape, dtype=torch.uint8, pin_memory=True)
+        hc.copy_(c)
+        hs.copy_(sc)
+        host[w] = (hc, hs)
+    torch.cuda.synchronize()
+    log(f"host store pinned in {time.time() - t0:.1f}s")
+    nx = len(xs)
+    warm = max(1, n_slots // sh.k)
+    cf = k3.CachedForward(xs[0], wr, host, n_slots, sh.k)
+    for i in range(warm):
+        cf.set_x(xs[(nx - 1 - i) % nx])
+        cf()
+    torch.cuda.synchronize()
+    before = cf.read()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        cf.set_x(xs[i % nx])
+        cf()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    after = cf.read()
+    hits, misses = after["hits"] - before["hits"], after["misses"] - before["misses"]
+    # the same selections replayed by the oracle (routing is deterministic)
+    fr = k3.Forward(xs[0], wr, experts, sh.k)
+    trace = []
+    for i in list(range(warm)) + list(range(steps)):
+        fr.set_x(xs[(nx - 1 - i) % nx] if len(trace) < warm else xs[i % nx])
+        fr.run_route()
+        trace.append(fr.route["topk_idx"].cpu().numpy().ravel().tolist())
+    lru = oc.lru_replay(trace, n_slots)
+    lru_h = sum(r["hits"] for r in lru[warm:])
+    total_all = sum(r["hits"] + r["misses"] for r in lru)
+    opt_h_all, _ = oc.opt_replay(trace, n_slots)
+    ms = elapsed * 1e3 / steps
+    miss_bytes = misses * sh.expert_bytes / steps
+    del cf, fr, host
+    return {"slots": n_slots, "hbm_bytes": n_slots * sh.expert_bytes, "host_store_bytes": sh.E * sh.expert_bytes,
+            "policy": "step-batched LRU", "warmup_steps": warm, "steps": steps, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(1e3 / ms, 1), "hit_rate": round(hits / max(1, hits + misses), 4),
+            "misses_per_step": round(misses / steps, 3), "host_link_bytes_per_step": round(miss_bytes),
+            "host_link_GBps": round(miss_bytes / (ms * 1e-3) / 1e9, 2),
+            "oracle_lru_hit_rate": round(lru_h / max(1, hits + misses), 4),
+            "whole_trace": {"steps": len(trace), "lru_hit_rate": round(sum(r["hits"] for r in lru) / total_all, 4),
+                            "belady_hit_rate": round(opt_h_all / total_all, 4)},
+            "trace": "the timed tokens' own selections (uniform routing: no reuse beyond chance)"}
 
 
 def measured_traffic(workload):

@@ -209,6 +209,57 @@ int k3moe_forward_noalloc(const k3moe_dims *dims, const float *x, const float *w
                           int32_t *perm_pair, int32_t *row_of_pair, float *y,
                           const k3moe_debug *dbg, hipStream_t stream);
 
+/* ---- HBM cache of experts in front of a host-memory store ----------------
+ * For layers whose experts do not all stay in HBM: the pages' engine keeps
+ * hot experts in a bounded memory with least-recently-used eviction and
+ * fetches a step's missing experts together before its matrix work
+ * (fiv.co.kr "kimi-k3-in-c deep dive", "four reductions", expert LRU cache
+ * paragraph).  Here every expert lives in host memory that the GPU can read
+ * (hipHostMalloc'd), n_slots experts' worth of HBM holds the resident ones,
+ * and the policy runs on the GPU in stream order (no host synchronisation):
+ *   - a step needs the distinct experts of its selection; resident ones hit;
+ *   - misses, in ascending expert id, take the slots that come first in
+ *     recency order among the slots the step does not hit (empty slots
+ *     first, lowest index first, then least recently used);
+ *   - every slot the step touches becomes most recent, those of one step
+ *     ordered by slot index.
+ * cache_state: device memory of k3moe_cache_state_bytes(E, n_slots) bytes,
+ * 256-byte aligned, owned by the caller, set up by k3moe_cache_reset (all
+ * slots empty); each k3moe_forward_cached call updates it.  One cache state
+ * serves one stream at a time.  E <= 1024, 1 <= n_slots <= E (else EINVAL /
+ * ENOTSUP). */
+int k3moe_cache_state_bytes(int E, int n_slots, size_t *bytes);
+int k3moe_cache_reset(void *cache_state, int E, int n_slots, hipStream_t stream);
+
+/* k3moe_forward with the experts behind the cache:
+ *   host_experts  all E experts (layout of k3moe_experts) in pinned host
+ *                 memory (hipHostMalloc'd, which the device reads over the
+ *                 host link; other memory: K3MOE_EHIP before any launch);
+ *                 never written
+ *   slot_experts  n_slots experts' worth of device memory in the same layout
+ *                 (slot s where expert s would be); the library writes it
+ *   cache_state   as above, for this E and n_slots
+ * Every array of both must be 16-byte aligned.  T * k <= n_slots (a step's
+ * experts must fit at once: EINVAL otherwise).  Per call: routing as
+ * k3moe_route; the policy update; a copy of the step's missed experts from
+ * host_experts into their slots over the host link; the expert FFN on the
+ * slots.  y and every routing output equal k3moe_forward's on host_experts'
+ * weights bit for bit.  No dbg.  ws as k3moe_forward. */
+int k3moe_forward_cached(const k3moe_dims *dims, const float *x, const float *w_router,
+                         const float *bias, int bias_mode, int score_fn,
+                         const k3moe_experts *host_experts, const k3moe_experts *slot_experts,
+                         int n_slots, void *cache_state, int act_mode, int32_t *topk_idx,
+                         float *topk_w, int32_t *counts, int32_t *offsets, int32_t *perm_pair,
+                         int32_t *row_of_pair, float *y, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* Copy the cache state to host memory (each output may be NULL) and wait
+ * for the stream: stats int64[4] = steps, hits, misses, misses of the last
+ * step; slot_of int32[E] (slot of each expert, -1 if not resident);
+ * expert_in int32[n_slots] (expert in each slot, -1 if empty). */
+int k3moe_cache_read(const void *cache_state, int E, int n_slots, int64_t *stats, int32_t *slot_of,
+                     int32_t *expert_in, hipStream_t stream);
+
 /* Human-readable text of a status code (static storage). */
 const char *k3moe_status_string(int status);
 

@@ -23,6 +23,7 @@ K3MOE_ACT_FP32, K3MOE_ACT_MXFP4 = 0, 1
 K3MOE_SCORE_SOFTMAX, K3MOE_SCORE_SIGMOID = 0, 1
 
 EXPORTS = ("k3moe_workspace_size", "k3moe_route", "k3moe_ffn", "k3moe_forward", "k3moe_forward_noalloc",
+           "k3moe_cache_state_bytes", "k3moe_cache_reset", "k3moe_forward_cached", "k3moe_cache_read",
            "k3moe_status_string", "k3moe_last_hip_error")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # K3MOE_NOALLOC_SCRATCH_BYTES
 
@@ -77,10 +78,16 @@ def _lib():
                                     ctypes.POINTER(Debug), P, SZ, P]
         L.k3moe_forward_noalloc.argtypes = [DP, P, P, P, I, I, ctypes.POINTER(Experts), I, P, P, P, P, P, P, P,
                                             ctypes.POINTER(Debug), P]
+        L.k3moe_cache_state_bytes.argtypes = [I, I, ctypes.POINTER(SZ)]
+        L.k3moe_cache_reset.argtypes = [P, I, I, P]
+        L.k3moe_forward_cached.argtypes = [DP, P, P, P, I, I, ctypes.POINTER(Experts), ctypes.POINTER(Experts), I, P,
+                                           I, P, P, P, P, P, P, P, P, SZ, P]
+        L.k3moe_cache_read.argtypes = [P, I, I, P, P, P, P]
         L.k3moe_status_string.argtypes = [I]
         L.k3moe_status_string.restype = ctypes.c_char_p
         L.k3moe_last_hip_error.argtypes = []
         for name in ("k3moe_workspace_size", "k3moe_route", "k3moe_ffn", "k3moe_forward", "k3moe_forward_noalloc",
+                     "k3moe_cache_state_bytes", "k3moe_cache_reset", "k3moe_forward_cached", "k3moe_cache_read",
                      "k3moe_last_hip_error"):
             getattr(L, name).restype = I
         _L = L
@@ -114,17 +121,25 @@ def _need(t, dtype, shape, name):
                          f"got {t.dtype} {tuple(t.shape)} on {t.device}")
 
 
-def make_experts(experts: dict, E: int, d: int, f: int) -> Experts:
+def make_experts(experts: dict, E: int, d: int, f: int, host: bool = False) -> Experts:
     """{'gate': (codes, scales), 'up': ..., 'down': ...} of uint8 cuda tensors
     ([E, f, d/2] + [E, f, d/32] for gate/up, [E, d, f/2] + [E, d, f/32] for
-    down) -> the C struct."""
+    down) -> the C struct.  host=True: pinned CPU tensors instead (the host
+    store of the expert cache; pinned memory is readable by the device at its
+    host address)."""
     shp = {"gate": (f, d), "up": (f, d), "down": (d, f)}
     mats = []
     for w in ("gate", "up", "down"):
         c, s = experts[w]
         rows, cols = shp[w]
-        _need(c, torch.uint8, (E, rows, cols // 2), f"{w}.codes")
-        _need(s, torch.uint8, (E, rows, cols // 32), f"{w}.scales")
+        if host:
+            for t, n, sh in ((c, "codes", (E, rows, cols // 2)), (s, "scales", (E, rows, cols // 32))):
+                if t.dtype != torch.uint8 or tuple(t.shape) != sh or not t.is_contiguous() or t.is_cuda \
+                        or not t.is_pinned():
+                    raise ValueError(f"{w}.{n}: expected a contiguous pinned uint8 CPU tensor of shape {sh}")
+        else:
+            _need(c, torch.uint8, (E, rows, cols // 2), f"{w}.codes")
+            _need(s, torch.uint8, (E, rows, cols // 32), f"{w}.scales")
         mats.append(MX(c.data_ptr(), s.data_ptr()))
     return Experts(*mats)
 
@@ -290,3 +305,75 @@ def k3moe_forward_noalloc(x, w_router, experts, k, bias=None, bias_mode="none", 
                                       ctypes.byref(dstruct) if dstruct is not None else None, _stream(stream))
     _check(rc, "k3moe_forward_noalloc")
     return y, route
+
+
+# ---- HBM expert cache ---------------------------------------------------------
+def k3moe_cache_state_bytes(E: int, n_slots: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib().k3moe_cache_state_bytes(E, n_slots, ctypes.byref(n)), "k3moe_cache_state_bytes")
+    return n.value
+
+
+class CachedForward:
+    """k3moe_forward_cached bound to fixed buffers: the experts of a layer in
+    pinned host memory (``host_experts``, same dict layout as the device
+    experts but pinned CPU tensors), ``n_slots`` experts' worth of HBM slots
+    and the cache state, all allocated here; ``reset`` empties the cache,
+    ``__call__`` runs one step (routing, policy update, copy of the missed
+    experts, expert FFN) and returns y; ``read`` returns the cache state."""
+
+    def __init__(self, x, w_router, host_experts, n_slots, k, bias=None, bias_mode="none", act_mode="fp32",
+                 stream=None, score_fn="softmax"):
+        T, d = x.shape
+        E = w_router.shape[0]
+        f = host_experts["gate"][0].shape[1]
+        _need(x, torch.float32, (T, d), "x")
+        _need(w_router, torch.float32, (E, d), "w_router")
+        if bias is not None:
+            _need(bias, torch.float32, (E,), "bias")
+        dev = x.device
+        self.E, self.n_slots = E, n_slots
+        self.dims = Dims(T, E, k, d, f)
+        self.host = make_experts(host_experts, E, d, f, host=True)
+        shp = {"gate": (f, d), "up": (f, d), "down": (d, f)}
+        self.slots = {w: (torch.empty((n_slots, r, c // 2), dtype=torch.uint8, device=dev),
+                          torch.empty((n_slots, r, c // 32), dtype=torch.uint8, device=dev))
+                      for w, (r, c) in shp.items()}
+        self.slot_struct = make_experts(self.slots, n_slots, d, f)
+        self.state = torch.empty(max(k3moe_cache_state_bytes(E, n_slots), 256), dtype=torch.uint8, device=dev)
+        self.route = alloc_route(T, E, k, dev)
+        self.y = torch.empty((T, d), dtype=torch.float32, device=dev)
+        self.ws = alloc_workspace(T, E, k, d, f, act_mode, dev)
+        self._keep = [x, w_router, bias, host_experts]
+        self._x, self._wr, self._bias = _ptr(x), _ptr(w_router), _ptr(bias)
+        self._bias_mode, self._score, self._act = _BIAS[bias_mode], _SCORE[score_fn], _ACT[act_mode]
+        self._r = [_ptr(self.route[n]) for n in ("topk_idx", "topk_w", "counts", "offsets", "perm_pair",
+                                                 "row_of_pair")]
+        self.stream = stream
+        self.reset()
+
+    def set_x(self, x):
+        _need(x, torch.float32, (self.dims.T, self.dims.d_model), "x")
+        self._x = _ptr(x)
+        self._keep[0] = x
+
+    def reset(self):
+        _check(_lib().k3moe_cache_reset(_ptr(self.state), self.E, self.n_slots, _stream(self.stream)),
+               "k3moe_cache_reset")
+
+    def __call__(self):
+        rc = _lib().k3moe_forward_cached(ctypes.byref(self.dims), self._x, self._wr, self._bias, self._bias_mode,
+                                         self._score, ctypes.byref(self.host), ctypes.byref(self.slot_struct),
+                                         self.n_slots, _ptr(self.state), self._act, *self._r, _ptr(self.y),
+                                         _ptr(self.ws), self.ws.numel(), _stream(self.stream))
+        _check(rc, "k3moe_forward_cached")
+        return self.y
+
+    def read(self) -> dict:
+        stats = (ctypes.c_int64 * 4)()
+        slot_of = (ctypes.c_int32 * self.E)()
+        expert_in = (ctypes.c_int32 * self.n_slots)()
+        _check(_lib().k3moe_cache_read(_ptr(self.state), self.E, self.n_slots, stats, slot_of, expert_in,
+                                       _stream(self.stream)), "k3moe_cache_read")
+        return {"steps": stats[0], "hits": stats[1], "misses": stats[2], "last_misses": stats[3],
+                "slot_of": list(slot_of), "expert_in": list(expert_in)}

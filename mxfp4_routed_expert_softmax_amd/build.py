@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libk3moe.so")
-SOURCES = ["api.hip", "route.hip", "gemv.hip", "mx.hip", "slices.hip"]
+SOURCES = ["api.hip", "route.hip", "gemv.hip", "mx.hip", "slices.hip", "cache.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

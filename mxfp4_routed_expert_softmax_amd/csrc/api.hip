@@ -221,7 +221,7 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
                         const int32_t* topk_idx, const float* topk_w, const int32_t* offsets,
                         const int32_t* perm_pair, const int32_t* row_of_pair, int act_mode,
                         float* y, const k3moe_debug* dbg, char* ws, const WsLayout& L,
-                        hipStream_t s)
+                        hipStream_t s, const int32_t* slot_of = nullptr, const int32_t* pair_slot = nullptr)
 {
     FfnArgs a{};
     a.T = dm->T;
@@ -242,6 +242,8 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
     a.offsets = offsets;
     a.perm_pair = perm_pair;
     a.row_of_pair = row_of_pair;
+    a.slot_of = slot_of;
+    a.pair_w = pair_slot ? pair_slot : topk_idx;
     const bool pair_path = act_mode == K3MOE_ACT_FP32 && use_pair_path(a);
     if (pair_path) {
         a.active = nullptr;  // slots are pairs
@@ -431,6 +433,123 @@ int k3moe_forward_noalloc(const k3moe_dims* dims, const float* x, const float* w
     if ((rc = scratch_ptr(&ws))) return rc;
     return k3moe_forward(dims, x, w_router, bias, bias_mode, score_fn, experts, act_mode, topk_idx, topk_w, counts,
                          offsets, perm_pair, row_of_pair, y, dbg, ws, K3MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+// ------------------------------------------------------- expert cache ---
+static int check_cache_dims(int E, int n_slots)
+{
+    if (E < 1 || n_slots < 1 || n_slots > E) return K3MOE_EINVAL;
+    if (E > 1024) return K3MOE_ENOTSUP;  // the policy kernel is one 1024-thread block
+    return K3MOE_OK;
+}
+
+int k3moe_cache_state_bytes(int E, int n_slots, size_t* bytes)
+{
+    int rc = check_cache_dims(E, n_slots);
+    if (rc) return rc;
+    if (!bytes) return K3MOE_EINVAL;
+    *bytes = cache_state_bytes(E, n_slots);
+    return K3MOE_OK;
+}
+
+int k3moe_cache_reset(void* cache_state, int E, int n_slots, hipStream_t stream)
+{
+    int rc = check_cache_dims(E, n_slots);
+    if (rc) return rc;
+    if (!cache_state || !aligned(cache_state, 256)) return K3MOE_EINVAL;
+    if ((rc = check_device())) return rc;
+    launch_cache_reset(cache_state_view(cache_state, E, n_slots), stream);
+    return finish_launches();
+}
+
+static int check_cache_experts(const k3moe_experts* e)
+{
+    if (!e) return K3MOE_EINVAL;
+    int rc;
+    if ((rc = check_mx(e->gate)) || (rc = check_mx(e->up)) || (rc = check_mx(e->down))) return rc;
+    // the copy moves 16-byte pieces of every array
+    if (!aligned(e->gate.scales, 16) || !aligned(e->up.scales, 16) || !aligned(e->down.scales, 16))
+        return K3MOE_EINVAL;
+    return K3MOE_OK;
+}
+
+int k3moe_forward_cached(const k3moe_dims* dims, const float* x, const float* w_router, const float* bias,
+                         int bias_mode, int score_fn, const k3moe_experts* host_experts,
+                         const k3moe_experts* slot_experts, int n_slots, void* cache_state, int act_mode,
+                         int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm_pair,
+                         int32_t* row_of_pair, float* y, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    int rc = check_dims(dims);
+    if (rc) return rc;
+    if ((rc = check_mode_act(act_mode))) return rc;
+    if ((rc = check_cache_dims(dims->E, n_slots))) return rc;
+    if ((int64_t)dims->T * dims->k > n_slots) return K3MOE_EINVAL;  // a step's experts must all fit
+    if (!cache_state || !aligned(cache_state, 256)) return K3MOE_EINVAL;
+    if ((rc = check_cache_experts(host_experts)) || (rc = check_cache_experts(slot_experts))) return rc;
+    rc = validate_route(dims, x, w_router, bias, bias_mode, score_fn, topk_idx, topk_w, counts, offsets,
+                        perm_pair, row_of_pair, ws, ws_bytes, act_mode);
+    if (rc) return rc;
+    rc = validate_ffn(dims, x, slot_experts, topk_idx, topk_w, counts, offsets, perm_pair, row_of_pair,
+                      act_mode, y, ws, ws_bytes);
+    if (rc || dims->T == 0) return rc;
+    if ((rc = check_device())) return rc;
+    const int E = dims->E, d = dims->d_model, f = dims->d_ff;
+    WsLayout L = ws_layout(dims->T, E, dims->k, d, f, act_mode);
+    char* w = static_cast<char*>(ws);
+    const CacheState cs = cache_state_view(cache_state, E, n_slots);
+    CacheCopy cp{};
+    const k3moe_mx* hs[3] = {&host_experts->gate, &host_experts->up, &host_experts->down};
+    const k3moe_mx* ds[3] = {&slot_experts->gate, &slot_experts->up, &slot_experts->down};
+    for (int m = 0; m < 3; ++m) {
+        // the device's address of each host array (pinned host memory is
+        // mapped for the device; anything else is refused here, before any
+        // kernel could touch it)
+        for (int q = 0; q < 2; ++q) {
+            const uint8_t* hp = q ? hs[m]->scales : hs[m]->codes;
+            void* dp = nullptr;
+            const hipError_t err = hipHostGetDevicePointer(&dp, const_cast<uint8_t*>(hp), 0);
+            if (err != hipSuccess || !dp) {
+                g_last_hip_error = err != hipSuccess ? (int)err : (int)hipErrorInvalidValue;
+                return K3MOE_EHIP;
+            }
+            cp.src[2 * m + q] = static_cast<const uint8_t*>(dp);
+        }
+        cp.dst[2 * m] = const_cast<uint8_t*>(ds[m]->codes);
+        cp.dst[2 * m + 1] = const_cast<uint8_t*>(ds[m]->scales);
+        cp.seg_bytes[2 * m] = (size_t)d * f / 2;
+        cp.seg_bytes[2 * m + 1] = (size_t)d * f / 32;
+    }
+    const int P = dims->T * dims->k;
+    enqueue_route(dims, x, w_router, bias, bias_mode, score_fn, topk_idx, topk_w, counts, offsets, perm_pair,
+                  row_of_pair, w, L, stream);
+    launch_cache_update(cs, P, topk_idx, stream);
+    launch_cache_fill(cs, cp, P < n_slots ? P : n_slots, stream);
+    rc = enqueue_ffn(dims, x, slot_experts, topk_idx, topk_w, offsets, perm_pair, row_of_pair, act_mode, y, nullptr,
+                     w, L, stream, cs.slot_of, cs.pair_slot);
+    return rc ? rc : finish_launches();
+}
+
+int k3moe_cache_read(const void* cache_state, int E, int n_slots, int64_t* stats, int32_t* slot_of,
+                     int32_t* expert_in, hipStream_t stream)
+{
+    int rc = check_cache_dims(E, n_slots);
+    if (rc) return rc;
+    if (!cache_state || !aligned(cache_state, 256)) return K3MOE_EINVAL;
+    if ((rc = check_device())) return rc;
+    const CacheState cs = cache_state_view(const_cast<void*>(cache_state), E, n_slots);
+    hipError_t err = hipSuccess;
+    if (stats) err = hipMemcpyAsync(stats, cs.hdr, 4 * sizeof(int64_t), hipMemcpyDeviceToHost, stream);
+    if (slot_of && err == hipSuccess)
+        err = hipMemcpyAsync(slot_of, cs.slot_of, (size_t)E * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (expert_in && err == hipSuccess)
+        err = hipMemcpyAsync(expert_in, cs.expert_in, (size_t)n_slots * sizeof(int32_t), hipMemcpyDeviceToHost,
+                             stream);
+    if (err == hipSuccess) err = hipStreamSynchronize(stream);
+    if (err != hipSuccess) {
+        g_last_hip_error = (int)err;
+        return K3MOE_EHIP;
+    }
+    return K3MOE_OK;
 }
 
 const char* k3moe_status_string(int status)

@@ -185,10 +185,12 @@ void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h, uint8_t* __restrict__ 
     int e, r_beg, n_e;
     if (PAIR) {
         r_beg = blockIdx.y;
-        e = a.topk_idx[r_beg];
+        e = a.pair_w[r_beg];  // weight index (the expert, or its cache slot)
         n_e = 1;
     } else if (!slot_expert(a, blockIdx.y, e, r_beg, n_e)) {
         return;
+    } else {
+        e = wslot(a, e);
     }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r0 = blockIdx.x * kGuRows;
@@ -306,7 +308,7 @@ void gateup_gemv_tokens_kernel(FfnArgs a, float* __restrict__ h)
     const int r0 = blockIdx.x * kGuRows;
     const int d = a.d, nb = d >> 5;
     const size_t crow = (size_t)(d >> 1), srow = (size_t)nb;
-    const size_t wrow0 = (size_t)e * a.f + r0;
+    const size_t wrow0 = (size_t)wslot(a, e) * a.f + r0;
     const int npairs = min(kGuRows, a.f - r0);  // multiple of 8 (f % 32 == 0)
     const __amdgpu_buffer_rsrc_t rg = weight_rsrc(a.gc + wrow0 * crow);
     const __amdgpu_buffer_rsrc_t ru = weight_rsrc(a.uc + wrow0 * crow);
@@ -433,7 +435,7 @@ void down_gemv_kernel(FfnArgs a, const float* __restrict__ hbuf,
     const int f = a.f, nb = f >> 5;
     const size_t crow = (size_t)(f >> 1), srow = (size_t)nb;
     const bool live = c0 < a.d;  // d % 16 == 0: a team's rows are all in or all out
-    const size_t wrow0 = (size_t)e * a.d + (live ? c0 : 0);
+    const size_t wrow0 = (size_t)wslot(a, e) * a.d + (live ? c0 : 0);
     const __amdgpu_buffer_rsrc_t rd = weight_rsrc(a.dc + wrow0 * crow);
     const __amdgpu_buffer_rsrc_t rds = weight_rsrc(a.ds + wrow0 * srow);
     uint32_t coff[BPL], soffl[BPL];
@@ -553,7 +555,7 @@ __global__ __launch_bounds__(64 * kGatherWaves) void down_gather_kernel(FfnArgs 
     for (int bt = 0; bt < NBT; ++bt) yacc[bt] = 0.f;
     for (int j = wave; j < k; j += kGatherWaves) {
         const int p = t * k + j;
-        const int e = a.topk_idx[p];
+        const int e = a.pair_w[p];  // weight index (the expert, or its cache slot)
         const float w = a.topk_w[p];
         const size_t wrow0 = (size_t)e * a.d + c0;
         const __amdgpu_buffer_rsrc_t rd = weight_rsrc(a.dc + wrow0 * crow);

@@ -98,7 +98,21 @@ struct FfnArgs {
     // block per (slot, tile) running all of the slot's passes.
     const int32_t* passes;
     int pstride;
+    // HBM expert cache: weights of expert e sit at slot slot_of[e] of the
+    // weight arrays (null: at e itself)
+    const int32_t* slot_of;
+    // weight index of pair p for the pair-major kernels: topk_idx itself, or
+    // (expert cache) the slot of that pair's expert -- one load, no branch, in
+    // kernels that run at the edge of their register budget
+    const int32_t* pair_w;
 };
+
+// Index of expert e's weights in the weight arrays
+__device__ __forceinline__ int wslot(const FfnArgs& a, int e)
+{
+    // e is block-uniform everywhere this is used: keep the lookup scalar
+    return __builtin_amdgcn_readfirstlane(a.slot_of ? a.slot_of[e] : e);
+}
 // Batches with at most kPairMajorMax token-expert pairs (and d_ff <= 8192)
 // take the pair-major path: gate/up per pair, then down with the combine
 // fused (launch_down_gather); larger ones are grouped by expert.
@@ -131,5 +145,36 @@ void launch_zero(float* y, size_t n, hipStream_t s);
 // per-pair rows into o [T*k][d] (grouped order) for launch_combine
 void launch_down_mfma(const FfnArgs& a, const uint8_t* hq_codes, const uint8_t* hq_scales, float* o,
                       hipStream_t s);
+
+// ---- HBM expert cache (cache.hip) -------------------------------------------
+struct CacheLayout {
+    size_t hdr;        // int64 [4]: steps, hits, misses, misses of the last step
+    size_t slot_of;    // int32 [E]: slot of expert e, -1 when not resident
+    size_t expert_in;  // int32 [S]: expert in slot s, -1 when empty
+    size_t order;      // int32 [S]: slots, least recently used first
+    size_t miss_e;     // int32 [S]: the last step's missed experts (ascending id)
+    size_t miss_s;     // int32 [S]: the slot each of them took
+    size_t pair_slot;  // int32 [S]: the last step's slot of each pair's expert (P <= S)
+    size_t total;
+};
+struct CacheState {
+    int E, S;
+    int64_t* hdr;
+    int32_t *slot_of, *expert_in, *order, *miss_e, *miss_s, *pair_slot;
+};
+// where to copy a missed expert from and to: six segments (gate codes, gate
+// scales, up codes, up scales, down codes, down scales) of seg_bytes[j] per
+// expert, expert e at src[j] + e * seg_bytes[j], slot s at dst[j] + s * seg_bytes[j]
+struct CacheCopy {
+    const uint8_t* src[6];
+    uint8_t* dst[6];
+    size_t seg_bytes[6];
+};
+CacheLayout cache_layout(int E, int S);
+size_t cache_state_bytes(int E, int S);
+CacheState cache_state_view(void* base, int E, int S);
+void launch_cache_reset(const CacheState& c, hipStream_t s);
+void launch_cache_update(const CacheState& c, int P, const int32_t* topk_idx, hipStream_t s);
+void launch_cache_fill(const CacheState& c, const CacheCopy& cp, int max_miss, hipStream_t s);
 
 }  // namespace k3

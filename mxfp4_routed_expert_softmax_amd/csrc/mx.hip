@@ -325,7 +325,7 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(FfnArgs a, const uint8
     const uint8_t* bc[2];
     const uint8_t* bs[2];
     {
-        const size_t wr = (size_t)e * a.f + nrow_w + li;
+        const size_t wr = (size_t)wslot(a, e) * a.f + nrow_w + li;
         bc[0] = a.gc + wr * crow;
         bs[0] = a.gs + wr * srow;
         bc[1] = a.uc + wr * crow;
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(FfnArgs a, const uint8_t
     for (int s = 0; s < 2; ++s) {
         const int n = nw + 16 * s;
         sub_ok[s] = n < a.d;  // d % 32 == 0: 16-row subtiles are whole
-        const size_t wr = (size_t)e * a.d + (sub_ok[s] ? n : 0) + li;
+        const size_t wr = (size_t)wslot(a, e) * a.d + (sub_ok[s] ? n : 0) + li;
         bc[s] = a.dc + wr * crow;
         bs[s] = a.ds + wr * srow;
     }
@@ -667,14 +667,14 @@ __device__ __forceinline__ void gateup_mx_item(const FfnArgs& a, int e, int r_be
     const uint32_t crow = (uint32_t)(a.d >> 1), srow = (uint32_t)(a.d >> 5);
     // the block's weight scales: gate rows n0.. (64 rows), then up rows
     {
-        const size_t r0 = (size_t)e * a.f + n0;
+        const size_t r0 = (size_t)wslot(a, e) * a.f + n0;
         const int nb = kGuTile * (int)srow;
         lds_copy(a.gs + r0 * srow, lds_addr(lds) + 2u * kAStage, nb);
         lds_copy(a.us + r0 * srow, lds_addr(lds) + 2u * kAStage + (uint32_t)nb, nb);
     }
     BSrc B;
     {
-        const size_t wr = (size_t)e * a.f + (size_t)(n0 + 16 * wave);
+        const size_t wr = (size_t)wslot(a, e) * a.f + (size_t)(n0 + 16 * wave);
         B.rc[0] = weight_rsrc(a.gc + wr * crow);
         B.rc[1] = weight_rsrc(a.uc + wr * crow);
         B.voc = (uint32_t)li * crow + 16u * (uint32_t)g;
@@ -709,13 +709,13 @@ __device__ __forceinline__ void down_mx_item(const FfnArgs& a, int e, int r_beg,
     const int nw = dtile * kDnTile + wave * 32;
     const uint32_t crow = (uint32_t)(a.f >> 1), srow = (uint32_t)(a.f >> 5);
     // the block's weight scales: d rows dtile*128 .. +127
-    lds_copy(a.ds + ((size_t)e * a.d + (size_t)dtile * kDnTile) * srow, lds_addr(lds) + 2u * kAStage,
+    lds_copy(a.ds + ((size_t)wslot(a, e) * a.d + (size_t)dtile * kDnTile) * srow, lds_addr(lds) + 2u * kAStage,
              kDnTile * (int)srow);
     const bool sub_ok[2] = {true, true};  // d % 128 == 0
     BSrc B;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-        const size_t wr = (size_t)e * a.d + (size_t)(nw + 16 * s);
+        const size_t wr = (size_t)wslot(a, e) * a.d + (size_t)(nw + 16 * s);
         B.rc[s] = weight_rsrc(a.dc + wr * crow);
         B.bso[s] = (uint32_t)(32 * wave + 16 * s + li) * srow;
     }

@@ -259,7 +259,7 @@ __global__ __launch_bounds__(512) void down_slices_staged_kernel(FfnArgs a, cons
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
         const int pp = t * k + min(wave + 8 * mm, k - 1);
-        ex[mm] = __builtin_amdgcn_readfirstlane(a.topk_idx[pp]);
+        ex[mm] = __builtin_amdgcn_readfirstlane(a.pair_w[pp]);  // weight index (the expert, or its cache slot)
         wt[mm] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.topk_w[pp])));
     }
     auto pick = [&](const int (&v)[4], int m) { return m == 0 ? v[0] : m == 1 ? v[1] : m == 2 ? v[2] : v[3]; };

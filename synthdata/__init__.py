@@ -71,6 +71,10 @@ WIDE = LayerShape("wide_d8256", d=8256, f=2560, E=8, k=2, layer=5)
 # scaled by 2^EDGE_OEXP[c] (so h by about 2^(2 EDGE_OEXP[c])), and the down
 # scales undo that; the router rows carry 2^EDGE_XEXP[b] so logits stay O(1).
 EDGE = LayerShape("edge_fmt", d=1024, f=512, E=8, k=2, layer=6, fmt="edge")
+# Full-size experts (d_model 7168, d_ff 2048, top-16) but 64 of them: the
+# expert-cache tests stream whole experts over the host link without
+# generating the 21 GB layer.
+CACHE_E64 = LayerShape("cache_e64", d=7168, f=2048, E=64, k=16, layer=7)
 EDGE_XEXP = np.round(np.linspace(-77, 73, EDGE.d // 32)).astype(np.int64)
 EDGE_OEXP = np.round(np.linspace(-48, 50, EDGE.f // 32)).astype(np.int64)
 EDGE_ZERO_BYTES = (0, 1, 251, 252)  # scale bytes forced onto some all-zero-code blocks

@@ -173,3 +173,53 @@ def test_noalloc_refuses_dimensions_beyond_its_scratch_without_touching_the_gpu(
     assert lib.k3moe_forward_noalloc(ctypes.byref(z), *([None] * 3 + [0, 0, None, 0] + [None] * 9)) == 0
     # single-token decode fits
     assert _ws(1, 896, 16, 7168, 2048, 0)[1] <= k3.NOALLOC_SCRATCH_BYTES
+
+
+def test_cache_state_size_and_dimension_checks():
+    lib = k3.lib()
+    n = ctypes.c_size_t(0)
+    assert lib.k3moe_cache_state_bytes(896, 256, ctypes.byref(n)) == k3.K3MOE_OK
+    # header + slot_of[E] + five int32 arrays of n_slots, each 256-aligned
+    up = lambda b: (b + 255) // 256 * 256
+    assert n.value == up(32) + up(896 * 4) + 5 * up(256 * 4)
+    assert k3.k3moe_cache_state_bytes(16, 4) == up(32) + up(64) + 5 * up(16)
+    for E, S, rc in ((896, 0, k3.K3MOE_EINVAL), (16, 17, k3.K3MOE_EINVAL), (2048, 64, k3.K3MOE_ENOTSUP),
+                     (0, 1, k3.K3MOE_EINVAL)):
+        assert lib.k3moe_cache_state_bytes(E, S, ctypes.byref(n)) == rc
+    assert lib.k3moe_cache_state_bytes(16, 4, None) == k3.K3MOE_EINVAL
+    assert lib.k3moe_cache_reset(None, 16, 4, None) == k3.K3MOE_EINVAL
+    assert lib.k3moe_cache_reset(ctypes.c_void_p(0x10010), 16, 4, None) == k3.K3MOE_EINVAL  # not 256-aligned
+
+
+def test_forward_cached_rejects_bad_arguments_without_touching_the_gpu():
+    lib = k3.lib()
+    fake = ctypes.c_void_p(0x10000)
+    mx = k3.MX(0x10000, 0x10000)
+    ex = k3.Experts(mx, mx, mx)
+    state = ctypes.c_void_p(0x20000)
+    # x, w_router, bias, bias_mode, score_fn, host, slots, n_slots, state, act, 6 routing outputs, y, ws, ws_bytes, stream
+    T, E, k = 1, 896, 16
+    ws = _ws(T, E, k, 7168, 2048, 0)[1]
+
+    def call(dims, **kw):
+        a = dict(x=fake, wr=fake, bias=None, bm=0, sf=0, host=ctypes.byref(ex), slots=ctypes.byref(ex), ns=32,
+                 state=state, act=0, ws=ctypes.c_void_p(0x40000), wsn=ws)
+        a.update(kw)
+        return lib.k3moe_forward_cached(ctypes.byref(dims), a["x"], a["wr"], a["bias"], a["bm"], a["sf"], a["host"],
+                                        a["slots"], a["ns"], a["state"], a["act"], *([fake] * 6), fake, a["ws"],
+                                        a["wsn"], None)
+
+    d1 = k3.Dims(T, E, k, 7168, 2048)
+    assert call(d1, ns=15) == k3.K3MOE_EINVAL          # a step's 16 experts do not fit 15 slots
+    assert call(d1, ns=E + 1) == k3.K3MOE_EINVAL
+    assert call(d1, state=None) == k3.K3MOE_EINVAL
+    assert call(d1, state=ctypes.c_void_p(0x20010)) == k3.K3MOE_EINVAL
+    assert call(d1, host=None) == k3.K3MOE_EINVAL
+    bad = k3.Experts(k3.MX(0x10000, 0x10004), mx, mx)  # scales not 16-byte aligned
+    assert call(d1, slots=ctypes.byref(bad)) == k3.K3MOE_EINVAL
+    assert call(d1, act=9) == k3.K3MOE_ENOTSUP
+    assert call(d1, wsn=ws - 1) == k3.K3MOE_EWORKSPACE
+    assert call(k3.Dims(3, E, k, 7168, 2048)) == k3.K3MOE_EINVAL  # 48 pairs > 32 slots
+    assert call(k3.Dims(2, E, k, 7168, 2048)) == k3.K3MOE_EWORKSPACE  # 32 pairs fit; the workspace is for T = 1
+    z = k3.Dims(0, E, k, 7168, 2048)
+    assert call(z) == k3.K3MOE_OK
