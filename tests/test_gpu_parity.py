@@ -291,8 +291,9 @@ def _check_mx_split(x, ref, dbg, y, tokens, k, get=None, shape=None):
     assert_y_close(y[tokens], y_ref, "y")
 
 
-@pytest.mark.parametrize("T", [1, 37, 300, 1100])
+@pytest.mark.parametrize("T", [1, 37, 300, 1100, 2000])
 def test_tiny_mx_split_step(tiny, T):
+    """T = 2000: ~250 tokens per expert, three passes of up to 96 each."""
     sh = tiny["shape"]
     _log(f"tiny mx T={T}")
     x = synthdata.tokens(sh, T, first=5000 + T)
@@ -366,12 +367,13 @@ def test_small_forward_one_token(small, bias_mode):
         assert_y_close(y, oracle_y(x, ref, [0], small["get"]))
 
 
-@pytest.mark.parametrize("T", [1, 37, 600])
+@pytest.mark.parametrize("T", [1, 37, 600, 1200])
 def test_small_mx_split_step(small, T):
     """MXFP4 activations on layers whose d_model and d_ff are multiples of
     512: the pipelined grouped GEMMs with one, two and three K chunks (512,
     1024, 1536); T = 600 puts more than 96 tokens on an expert (several
-    passes per block)."""
+    passes per block); T = 1200 puts 200-300 tokens on an expert (three or
+    four passes of up to 96)."""
     sh = small["shape"]
     _log(f"{sh.name} mx T={T}")
     x = synthdata.tokens(sh, T, first=9000 + T)
