@@ -24,8 +24,10 @@
  * Conventions for every entry point:
  *  - Pointers named as device pointers must be device memory of the current
  *    HIP device (e.g. torch tensors); the caller owns all of them.  The
- *    library allocates nothing and keeps no state between calls except a
- *    per-device cache of "is this device gfx950".
+ *    library allocates nothing at run time.  Between calls it keeps only a
+ *    per-device record of "is this device gfx950" and, for
+ *    k3moe_forward_noalloc, its fixed per-device scratch array (part of the
+ *    loaded library); the expert cache's state is caller-owned memory.
  *  - Calls only enqueue work on `stream` and never synchronise; outputs are
  *    valid once the stream has completed that work.  Calls that share a
  *    workspace must be ordered on one stream.

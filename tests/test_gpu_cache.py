@@ -116,3 +116,43 @@ def test_cache_reset_empties_and_refuses_oversized_steps():
     x3 = torch.from_numpy(synthdata.tokens(sh, 3)).to(DEV)
     with pytest.raises(k3.K3MoEError):
         k3.CachedForward(x3, wr_dev, pinned, 4, sh.k)()  # 3 tokens x top-2 = 6 pairs > 4 slots
+
+
+def test_cache_step_replays_in_a_hip_graph():
+    """k3moe_forward_cached enqueues everything in stream order with no host
+    synchronisation, so a step can be captured and replayed: after the first
+    replay every expert of the (fixed) token is resident, later replays are
+    all hits and give the same y as the eager step."""
+    sh = synthdata.TINY
+    host = synthdata.all_experts_host(sh)
+    dev = {w: (torch.from_numpy(host[w][0]).to(DEV), torch.from_numpy(host[w][1]).to(DEV)) for w in host}
+    pinned = _pinned_copy(dev)
+    wr_dev = torch.from_numpy(synthdata.router_weight(sh)).to(DEV)
+    x = torch.from_numpy(synthdata.tokens(sh, 1, first=321)).to(DEV)
+    eager = k3.Forward(x, wr_dev, dev, sh.k)
+    eager()
+    torch.cuda.synchronize()
+    y_ref = eager.y.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    cf = k3.CachedForward(x, wr_dev, pinned, 4, sh.k, stream=s)
+    with torch.cuda.stream(s):
+        cf()  # warm-up call outside the capture
+    torch.cuda.synchronize()
+    cf.reset()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        cf()
+    torch.cuda.synchronize()
+    cf.reset()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        cf.y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cf.y, y_ref), f"replay {rep}: y differs from the eager k3moe_forward"
+        st = cf.read()
+        assert st["steps"] == rep + 1
+        assert st["misses"] == sh.k and st["hits"] == sh.k * rep  # misses on the first replay only
