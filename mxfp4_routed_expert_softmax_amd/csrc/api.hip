@@ -244,6 +244,7 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
     a.row_of_pair = row_of_pair;
     a.slot_of = slot_of;
     a.pair_w = pair_slot ? pair_slot : topk_idx;
+    a.o_stream = (size_t)a.P * a.d * sizeof(float) > ((size_t)128 << 20) ? 1 : 0;
     const bool pair_path = act_mode == K3MOE_ACT_FP32 && use_pair_path(a);
     if (pair_path) {
         a.active = nullptr;  // slots are pairs

@@ -635,7 +635,14 @@ __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a, const float* __
         }
         float4 v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = o4[(size_t)row[u] * d4 + c4];
+        for (int u = 0; u < 4; ++u) {
+            if (a.o_stream) {  // rows too large for the caches: read once, non-temporal
+                const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o4 + (size_t)row[u] * d4 + c4));
+                v[u] = make_float4(t[0], t[1], t[2], t[3]);
+            } else {
+                v[u] = o4[(size_t)row[u] * d4 + c4];
+            }
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             acc.x = __builtin_fmaf(w[u], v[u].x, acc.x);

@@ -101,6 +101,10 @@ struct FfnArgs {
     // HBM expert cache: weights of expert e sit at slot slot_of[e] of the
     // weight arrays (null: at e itself)
     const int32_t* slot_of;
+    // per-pair rows o of the grouped paths take non-temporal stores and loads
+    // (set when they outgrow the 256 MB last-level cache: written once, read
+    // once by the combine; smaller ones stay cached between the two kernels)
+    int o_stream;
     // weight index of pair p for the pair-major kernels: topk_idx itself, or
     // (expert cache) the slot of that pair's expert -- one load, no branch, in
     // kernels that run at the edge of their register budget

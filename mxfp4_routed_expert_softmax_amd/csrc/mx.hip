@@ -248,7 +248,7 @@ __device__ __forceinline__ void gateup_epilogue(const FfnArgs& a, const f32x4 (&
 
 // down: per-pair fp32 rows o (grouped order) for the deterministic combine;
 // subtile s of this wave covers d rows nw + 16*s .. +15
-template <int MT>
+template <int MT, bool NT>
 __device__ __forceinline__ void down_epilogue(const FfnArgs& a, const f32x4 (&c)[MT][2], int mt_n, int m0,
                                               int n_e, int r_beg, int nw, const bool (&sub_ok)[2], int li, int g,
                                               float* __restrict__ o)
@@ -262,8 +262,14 @@ __device__ __forceinline__ void down_epilogue(const FfnArgs& a, const f32x4 (&c)
             if (m < n_e) {
                 float* orow = o + (size_t)(r_beg + m) * a.d + nw + li;
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    if (sub_ok[s]) orow[16 * s] = c[mt][s][v];
+                for (int s = 0; s < 2; ++s) {
+                    if (sub_ok[s]) {
+                        if (NT)  // rows written once and read once (FfnArgs::o_stream)
+                            __builtin_nontemporal_store(c[mt][s][v], orow + 16 * s);
+                        else
+                            orow[16 * s] = c[mt][s][v];
+                    }
+                }
             }
         }
     }
@@ -398,7 +404,10 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(FfnArgs a, const uint8_t
 #pragma unroll
             for (int s = 0; s < 2; ++s) c[mt][s] = (f32x4){0.f, 0.f, 0.f, 0.f};
         gemm_pass128<2>(rows_c, rows_s, nrows, bc, bs, K, mt_n, li, g, c);
-        down_epilogue<kMT>(a, c, mt_n, m0, n_e, r_beg, nw, sub_ok, li, g, o);
+        if (a.o_stream)
+            down_epilogue<kMT, true>(a, c, mt_n, m0, n_e, r_beg, nw, sub_ok, li, g, o);
+        else
+            down_epilogue<kMT, false>(a, c, mt_n, m0, n_e, r_beg, nw, sub_ok, li, g, o);
         __syncthreads();  // rows_c / rows_s reused by the next pass
     }
 }
@@ -637,7 +646,10 @@ __device__ __forceinline__ void down_pass(const FfnArgs& a, const ASrc& A, const
 {
     f32x4 c[MT][2];
     gemm_pass512<MT>(A, B, cbase, sbase, a.f, a_read_offsets(li, g), lds, c);
-    down_epilogue<MT>(a, c, mt_n, m0, n_e, r_beg, nw, sub_ok, li, g, o);
+    if (a.o_stream)
+        down_epilogue<MT, true>(a, c, mt_n, m0, n_e, r_beg, nw, sub_ok, li, g, o);
+    else
+        down_epilogue<MT, false>(a, c, mt_n, m0, n_e, r_beg, nw, sub_ok, li, g, o);
 }
 
 // Every pass runs kPassMT tiles (a fixed set of accumulator registers;
