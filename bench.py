@@ -6,10 +6,13 @@ in HBM.  The default workload is single-token greedy decode on the
 896-expert / top-16 layer (d_model 7168, d_ff 2048), a fresh seeded token per
 step (1000 distinct tokens, cycled).
 
-Prints one JSON line: throughput in tokens/s, the expert-FFN stage against the
-HBM roofline (active-expert bytes / the stage's average duration, timed with
-HIP events on the launch stream), and the fp64 oracle timed on the host cores
-on a bounded sample of the same workload.
+Prints one JSON line: throughput in tokens/s; the roofline of the dominant
+kernel (its algorithmic bytes -- the active experts' weights it streams, the
+activations it reads, the outputs it writes -- over its average time, taken
+from HIP events that the library records on the launch stream after each
+kernel of the expert-FFN stage), with every kernel of the stage and the whole
+stage (timed by events around k3moe_ffn) beside it; and the fp64 oracle timed
+on the host cores on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -176,7 +179,9 @@ def main():
 def measure(k3, synthdata, torch, dev, wl, experts, wr, steps, warmup, use_graph):
     """Time `steps` steps of workload wl (after `warmup`), inputs resident.
     Every ev_every-th step issues k3moe_route and k3moe_ffn as two calls with
-    HIP events on the launch stream around the expert-FFN stage; the others
+    HIP events on the launch stream around the expert-FFN stage; as many
+    other steps (the same steps when every step carries events) have the
+    library record a mark event after each kernel of the stage; the rest
     issue k3moe_forward.  At least MIN_EV_SAMPLES steps carry events."""
     sh, T = wl.shape, wl.T
     bias = torch.from_numpy(synthdata.zipf_bias(sh)).to(dev) if wl.zipf_bias else None
@@ -189,17 +194,26 @@ def measure(k3, synthdata, torch, dev, wl, experts, wr, steps, warmup, use_graph
     fw = k3.Forward(xs[0], wr, experts, sh.k, bias, bias_mode, wl.act_mode)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i, ev=None, mk=None):
         fw.set_x(xs[i % nbatch])
-        if ev is None:
+        if ev is None and mk is None:
             fw()  # k3moe_forward: the whole layer in one C call
-        else:
+        elif mk is None:
             # the same work as two calls, HIP events on this stream around
             # the expert-FFN stage (k3moe_ffn)
             fw.run_route()
             ev[0].record(stream)
             fw.run_ffn()
             ev[1].record(stream)
+        else:
+            # the same, with a mark event after every kernel of the stage
+            fw.run_route()
+            mk[0].record(stream)
+            mk[1].set()
+            try:
+                fw.run_ffn()
+            finally:
+                k3.StageMarks.clear()
 
     for i in range(warmup):
         step(i)
@@ -225,14 +239,34 @@ def measure(k3, synthdata, torch, dev, wl, experts, wr, steps, warmup, use_graph
     # expert-FFN stage.  An event record costs a few microseconds of stream
     # time, so one-token steps (~0.1 ms) are marked one in EV_EVERY_DECODE
     # (more often when there are fewer than MIN_EV_SAMPLES * EV_EVERY_DECODE).
+    # Kernel marks (k3moe_set_stage_marks) go on other steps than the stage
+    # events when steps are short (their records would lengthen the stage),
+    # on the same steps otherwise.
     ev_every = max(1, min(EV_EVERY_DECODE if T == 1 else 1, steps // MIN_EV_SAMPLES))
     nev = (steps + ev_every - 1) // ev_every
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
+    mk_off = ev_every // 2 if ev_every > 1 else 0
+    nmk = len(range(mk_off, steps, ev_every)) if graph is None else 0
+    mks = [(torch.cuda.Event(enable_timing=True), k3.StageMarks(k3.MAX_MARKS, stream)) for _ in range(nmk)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     if graph is None:
         for i in range(steps):
-            step(i, evs[i // ev_every] if i % ev_every == 0 else None)
+            ev = evs[i // ev_every] if i % ev_every == 0 else None
+            mk = mks[i // ev_every] if i % ev_every == mk_off else None
+            if ev is not None and mk is not None:  # every step carries events: marks and stage together
+                fw.set_x(xs[i % nbatch])
+                fw.run_route()
+                ev[0].record(stream)
+                mk[0].record(stream)
+                mk[1].set()
+                try:
+                    fw.run_ffn()
+                finally:
+                    k3.StageMarks.clear()
+                ev[1].record(stream)
+            else:
+                step(i, ev, mk)
     else:
         for i in range(steps):
             gx.copy_(xs[i % nbatch], non_blocking=True)
@@ -250,20 +284,39 @@ def measure(k3, synthdata, torch, dev, wl, experts, wr, steps, warmup, use_graph
     roofline = None
     if graph is None:
         ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-        achieved = (expert_bytes + act_bytes) / (ffn_ms * 1e-3) / 1e9
+        kern = kernel_times(mks)
+        kb = kernel_bytes(sh, T, n_active, wl.act_mode)
+        stage = {"kernels": "every kernel k3moe_ffn launches", "bytes_per_launch": expert_bytes + act_bytes,
+                 "avg_ms": round(ffn_ms, 5), "event_samples": len(evs),
+                 "achieved": round((expert_bytes + act_bytes) / (ffn_ms * 1e-3) / 1e9, 1),
+                 "traffic": measured_traffic(wl.name)}
+        stage["frac"] = round(stage["achieved"] / HBM_PEAK_GBS, 4)
+        # the dominant kernel: the longest of the stage, timed by its marks
+        dom = max((n for n in kern if kb.get(n)), key=lambda n: kern[n]["avg_ms"])
+        per = {}
+        for n, v in kern.items():
+            b = kb.get(n)
+            per[n] = {"avg_ms": round(v["avg_ms"], 5), "bytes_per_launch": b}
+            if b:
+                per[n]["frac"] = round(b / (v["avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        achieved = kb[dom] / (kern[dom]["avg_ms"] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
-                    "kernel": "expert FFN stage (every kernel k3moe_ffn launches)",
-                    "bytes_per_launch": expert_bytes + act_bytes, "avg_ms": round(ffn_ms, 5),
-                    "event_samples": len(evs)}
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name, KERNEL_NAMES[dom]),
+                    "kernel": f"{dom} ({KERNEL_NAMES[dom]}*)", "bytes_per_launch": kb[dom],
+                    "avg_ms": round(kern[dom]["avg_ms"], 5), "event_samples": len(mks),
+                    "kernels": per, "stage": stage}
         # the whole layer per step (router weights + active experts + x, y) over the timed step time
         layer_bytes = sh.E * sh.d * 4 + expert_bytes + act_bytes
         roofline["layer"] = {"bytes_per_step": layer_bytes,
                              "frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         if wl.act_mode == "mxfp4":
             flops = 2.0 * 3 * sh.d * sh.f * T * sh.k
-            roofline["flops_per_launch"] = flops
-            roofline["mfma_frac"] = round(flops / (ffn_ms * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS, 4)
+            stage["flops_per_launch"] = flops
+            stage["mfma_frac"] = round(flops / (ffn_ms * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS, 4)
+            if dom == "gateup":
+                gflops = 2.0 * 2 * sh.d * sh.f * T * sh.k
+                roofline["flops_per_launch"] = gflops
+                roofline["mfma_frac"] = round(gflops / (kern[dom]["avg_ms"] * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS, 4)
     return dict(fw=fw, xs=xs, nbatch=nbatch, stream=stream, ms_per_step=ms_per_step,
                 tokens_per_s=tokens_per_s, roofline=roofline, n_active=n_active, bias_mode=bias_mode,
                 graph=graph)
@@ -330,8 +383,50 @@ def measure_cache(k3, synthdata, torch, wl, experts, wr, xs, n_slots, steps):
             "trace": "the timed tokens' own selections (uniform routing: no reuse beyond chance)"}
 
 
-def measured_traffic(workload):
-    """HBM bytes per expert-FFN launch from the committed counter profile
+# mark kinds -> the kernel name prefix in the profiles
+KERNEL_NAMES = {"active_list": "active_list", "quantize": "quantize_rows", "gateup": "gateup_",
+                "down": "down_", "down_combine": "down_", "combine": "combine_"}
+
+
+def kernel_times(mks):
+    """Mean time of each kernel of the stage over the marked steps: the
+    interval from the previous mark (the first: from the start event)."""
+    acc = {}
+    kinds = None
+    for start, m in mks:
+        ks = m.kinds()
+        if kinds is None:
+            kinds = ks
+        if ks != kinds:
+            raise RuntimeError(f"the stage launched different kernels across steps: {kinds} / {ks}")
+        prev = start
+        for i, n in enumerate(ks):
+            acc.setdefault(n, []).append(prev.elapsed_time(m.events[i]))
+            prev = m.events[i]
+    return {n: {"avg_ms": float(np.mean(v)), "samples": len(v)} for n, v in acc.items()}
+
+
+def kernel_bytes(sh, T, n_active, act_mode):
+    """Algorithmic bytes of each kernel of the stage: the active experts'
+    weights it streams once, the activations it reads and the outputs it
+    writes (h of the one-token path stays an on-chip intermediate of the
+    method and is not counted)."""
+    P, d, f = T * sh.k, sh.d, sh.f
+    w_gu = n_active * 2 * f * (d // 2 + d // 32)
+    w_dn = n_active * d * (f // 2 + f // 32)
+    mx_row = lambda n: n // 2 + n // 32  # noqa: E731  MXFP4 bytes of n values
+    if act_mode == "mxfp4":
+        return {"active_list": None, "quantize": T * d * 4 + T * mx_row(d),
+                "gateup": w_gu + T * mx_row(d) + P * mx_row(f),
+                "down": w_dn + P * mx_row(f) + P * d * 4,
+                "combine": P * d * 4 + T * d * 4}
+    return {"active_list": None, "gateup": w_gu + T * d * 4, "down_combine": w_dn + T * d * 4,
+            "down": w_dn + P * d * 4, "combine": P * d * 4 + T * d * 4}
+
+
+def measured_traffic(workload, prefix=None):
+    """HBM bytes per expert-FFN launch (or, with prefix, per launch of the
+    stage's kernel whose name holds it) from the committed counter profile
     (FETCH_SIZE / WRITE_SIZE scaled by a plain-copy calibration), or None
     when the kernel sources changed since those counters were taken."""
     import hashlib
@@ -347,7 +442,7 @@ def measured_traffic(workload):
     w = rec["workloads"][workload]
     total = 0.0
     for name, v in w["kernels"].items():
-        if any(key in name for key in FFN_KERNELS):
+        if (prefix in name) if prefix else any(key in name for key in FFN_KERNELS):
             total += (v["fetch_kib"] * w["fetch_scale"] + v["write_kib"] * w["write_scale"]) * 1024
     return round(total)
 

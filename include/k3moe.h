@@ -262,6 +262,29 @@ int k3moe_forward_cached(const k3moe_dims *dims, const float *x, const float *w_
 int k3moe_cache_read(const void *cache_state, int E, int n_slots, int64_t *stats, int32_t *slot_of,
                      int32_t *expert_in, hipStream_t stream);
 
+/* Kernel timing marks, a measurement aid (not part of the method): per host
+ * thread, every later expert-FFN stage (k3moe_ffn and the FFN half of
+ * k3moe_forward, k3moe_forward_noalloc, k3moe_forward_cached) records
+ * events[i] on its stream right after the i-th kernel it launches, for
+ * i < n, and writes that kernel's kind (K3MOE_KERNEL_*) to kinds[i] and the
+ * number of kernels the stage launched to *launched (kinds and launched are
+ * host memory, either may be NULL, and must stay valid while marks are set).
+ * With a start event recorded before the call, the interval up to mark i is
+ * kernel i's time on the stream.  events are hipEvent_t created by the
+ * caller; each record costs a few microseconds of stream time, so leave
+ * marks off outside timing runs, and do not set them while capturing a
+ * graph.  n == 0 switches marking off.  Errors: K3MOE_EINVAL for n < 0,
+ * n > K3MOE_MAX_MARKS or a NULL event (the marks are then unchanged); a
+ * failed record makes the FFN call return K3MOE_EHIP. */
+#define K3MOE_MAX_MARKS 8
+#define K3MOE_KERNEL_ACTIVE_LIST  1  /* active experts (and MXFP4 pass lists)   */
+#define K3MOE_KERNEL_QUANTIZE     2  /* MXFP4 activation quantiser               */
+#define K3MOE_KERNEL_GATEUP       3  /* gate/up product with SiLU(g)*u          */
+#define K3MOE_KERNEL_DOWN         4  /* down product into per-pair rows         */
+#define K3MOE_KERNEL_DOWN_COMBINE 5  /* down product with the combine fused     */
+#define K3MOE_KERNEL_COMBINE      6  /* gate-weighted combine of per-pair rows  */
+int k3moe_set_stage_marks(void *const *events, int n, int *kinds, int *launched);
+
 /* Human-readable text of a status code (static storage). */
 const char *k3moe_status_string(int status);
 

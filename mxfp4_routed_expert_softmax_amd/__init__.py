@@ -24,8 +24,10 @@ K3MOE_SCORE_SOFTMAX, K3MOE_SCORE_SIGMOID = 0, 1
 
 EXPORTS = ("k3moe_workspace_size", "k3moe_route", "k3moe_ffn", "k3moe_forward", "k3moe_forward_noalloc",
            "k3moe_cache_state_bytes", "k3moe_cache_reset", "k3moe_forward_cached", "k3moe_cache_read",
-           "k3moe_status_string", "k3moe_last_hip_error")
+           "k3moe_set_stage_marks", "k3moe_status_string", "k3moe_last_hip_error")
 NOALLOC_SCRATCH_BYTES = 64 << 20  # K3MOE_NOALLOC_SCRATCH_BYTES
+MAX_MARKS = 8  # K3MOE_MAX_MARKS
+KERNEL_KINDS = {1: "active_list", 2: "quantize", 3: "gateup", 4: "down", 5: "down_combine", 6: "combine"}
 
 _BIAS = {"none": K3MOE_BIAS_NONE, "logits": K3MOE_BIAS_LOGITS, "select_only": K3MOE_BIAS_SELECT_ONLY}
 _ACT = {"fp32": K3MOE_ACT_FP32, "mxfp4": K3MOE_ACT_MXFP4}
@@ -83,12 +85,13 @@ def _lib():
         L.k3moe_forward_cached.argtypes = [DP, P, P, P, I, I, ctypes.POINTER(Experts), ctypes.POINTER(Experts), I, P,
                                            I, P, P, P, P, P, P, P, P, SZ, P]
         L.k3moe_cache_read.argtypes = [P, I, I, P, P, P, P]
+        L.k3moe_set_stage_marks.argtypes = [ctypes.POINTER(P), I, P, P]
         L.k3moe_status_string.argtypes = [I]
         L.k3moe_status_string.restype = ctypes.c_char_p
         L.k3moe_last_hip_error.argtypes = []
         for name in ("k3moe_workspace_size", "k3moe_route", "k3moe_ffn", "k3moe_forward", "k3moe_forward_noalloc",
                      "k3moe_cache_state_bytes", "k3moe_cache_reset", "k3moe_forward_cached", "k3moe_cache_read",
-                     "k3moe_last_hip_error"):
+                     "k3moe_set_stage_marks", "k3moe_last_hip_error"):
             getattr(L, name).restype = I
         _L = L
     return _L
@@ -267,6 +270,41 @@ class Forward:
                                   self._ws, self._wsn, _stream(self.stream))
         _check(rc, "k3moe_forward")
         return self.y
+
+
+class StageMarks:
+    """Timing marks after the kernels of the expert-FFN stage
+    (k3moe_set_stage_marks).  ``set()`` makes this object's n events the
+    marks of this host thread, ``clear()`` switches marking off.  After a
+    marked call, ``events[i]`` follows kernel i, ``kinds()`` names those
+    kernels and ``launched`` is the number the stage launched."""
+
+    def __init__(self, n=MAX_MARKS, stream=None):
+        if not 1 <= n <= MAX_MARKS:
+            raise ValueError(f"1 <= n <= {MAX_MARKS}")
+        st = stream if stream is not None else torch.cuda.current_stream()
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in self.events:
+            e.record(st)  # the HIP event is created on the first record
+        self._handles = (ctypes.c_void_p * n)(*[e.cuda_event for e in self.events])
+        self._kinds = (ctypes.c_int * n)()
+        self._launched = ctypes.c_int(0)
+
+    def set(self):
+        rc = _lib().k3moe_set_stage_marks(self._handles, len(self.events), ctypes.cast(self._kinds, ctypes.c_void_p),
+                                          ctypes.c_void_p(ctypes.addressof(self._launched)))
+        _check(rc, "k3moe_set_stage_marks")
+
+    @staticmethod
+    def clear():
+        _check(_lib().k3moe_set_stage_marks(None, 0, None, None), "k3moe_set_stage_marks")
+
+    @property
+    def launched(self):
+        return self._launched.value
+
+    def kinds(self):
+        return [KERNEL_KINDS.get(self._kinds[i], "?") for i in range(min(self.launched, len(self.events)))]
 
 
 def k3moe_forward(x, w_router, experts, k, bias=None, bias_mode="none", act_mode="fp32", dbg=None,

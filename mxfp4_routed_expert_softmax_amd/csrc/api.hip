@@ -217,6 +217,38 @@ static void enqueue_route(const k3moe_dims* dm, const float* x, const float* w_r
                       row_of_pair, cert, s);
 }
 
+// Timing marks of the expert-FFN stage (a measurement aid, per host thread):
+// events recorded on the stream right after each kernel the stage launches.
+struct StageMarks {
+    hipEvent_t ev[K3MOE_MAX_MARKS];
+    int n;
+    int* kinds;     // host [n]: the kernel kind before each mark
+    int* launched;  // host: kernels the last stage launched
+};
+static thread_local StageMarks g_marks{};
+
+struct MarkCursor {
+    int i = 0;
+    hipError_t err = hipSuccess;
+    void operator()(int kind, hipStream_t s)
+    {
+        if (i < g_marks.n) {
+            if (g_marks.kinds) g_marks.kinds[i] = kind;
+            if (err == hipSuccess) err = hipEventRecord(g_marks.ev[i], s);
+        }
+        ++i;
+    }
+    int finish()
+    {
+        if (g_marks.launched) *g_marks.launched = i;
+        if (err != hipSuccess) {
+            g_last_hip_error = (int)err;
+            return K3MOE_EHIP;
+        }
+        return K3MOE_OK;
+    }
+};
+
 static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts* ex,
                         const int32_t* topk_idx, const float* topk_w, const int32_t* offsets,
                         const int32_t* perm_pair, const int32_t* row_of_pair, int act_mode,
@@ -246,6 +278,7 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
     a.pair_w = pair_slot ? pair_slot : topk_idx;
     a.o_stream = (size_t)a.P * a.d * sizeof(float) > ((size_t)128 << 20) ? 1 : 0;
     const bool pair_path = act_mode == K3MOE_ACT_FP32 && use_pair_path(a);
+    MarkCursor mark;
     if (pair_path) {
         a.active = nullptr;  // slots are pairs
         a.nslots = a.P;
@@ -259,6 +292,7 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
         int32_t* passes = reinterpret_cast<int32_t*>(ws + L.passes);
         a.pstride = pass_stride(a.E);
         launch_active_list(a.E, offsets, active, mx ? mx_tiles_per_pass() : 0, passes, a.pstride, s);
+        mark(K3MOE_KERNEL_ACTIVE_LIST, s);
         a.active = active;
         a.nslots = a.E;
         a.passes = mx ? passes : nullptr;
@@ -270,14 +304,21 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
             uint8_t* hsc = reinterpret_cast<uint8_t*>(ws + L.hs_codes);
             uint8_t* hss = reinterpret_cast<uint8_t*>(ws + L.hs_scales);
             launch_gateup_gemv_slices(a, hsc, hss, s);
+            mark(K3MOE_KERNEL_GATEUP, s);
             launch_down_slices(a, hsc, hss, y, s);
+            mark(K3MOE_KERNEL_DOWN_COMBINE, s);
         } else if (pair_path) {
             launch_gateup_gemv(a, h, s);
+            mark(K3MOE_KERNEL_GATEUP, s);
             launch_down_gather(a, h, y, s);
+            mark(K3MOE_KERNEL_DOWN_COMBINE, s);
         } else {
             launch_gateup_gemv(a, h, s);
+            mark(K3MOE_KERNEL_GATEUP, s);
             launch_down_gemv(a, h, o, s);
+            mark(K3MOE_KERNEL_DOWN, s);
             launch_combine(a, o, y, s);
+            mark(K3MOE_KERNEL_COMBINE, s);
         }
     } else {
         uint8_t* xqc = reinterpret_cast<uint8_t*>(ws + L.xq_codes);
@@ -285,6 +326,7 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
         uint8_t* hqc = reinterpret_cast<uint8_t*>(ws + L.hq_codes);
         uint8_t* hqs = reinterpret_cast<uint8_t*>(ws + L.hq_scales);
         launch_quantize_rows((long)a.T * (a.d / 32), x, xqc, xqs, s);
+        mark(K3MOE_KERNEL_QUANTIZE, s);
         hipError_t err = hipSuccess;
         if (dbg && dbg->x_codes && err == hipSuccess)
             err = hipMemcpyAsync(dbg->x_codes, xqc, (size_t)a.T * a.d / 2, hipMemcpyDeviceToDevice, s);
@@ -296,14 +338,29 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
         }
         launch_gateup_mfma(a, xqc, xqs, hqc, hqs, dbg ? dbg->h : nullptr,
                            dbg ? dbg->h_codes : nullptr, dbg ? dbg->h_scales : nullptr, s);
+        mark(K3MOE_KERNEL_GATEUP, s);
         float* o = reinterpret_cast<float*>(ws + L.o);
         launch_down_mfma(a, hqc, hqs, o, s);
+        mark(K3MOE_KERNEL_DOWN, s);
         launch_combine(a, o, y, s);
+        mark(K3MOE_KERNEL_COMBINE, s);
     }
-    return K3MOE_OK;
+    return mark.finish();
 }
 
 extern "C" {
+
+int k3moe_set_stage_marks(void* const* events, int n, int* kinds, int* launched)
+{
+    if (n < 0 || n > K3MOE_MAX_MARKS || (n > 0 && !events)) return K3MOE_EINVAL;
+    for (int i = 0; i < n; ++i)
+        if (!events[i]) return K3MOE_EINVAL;
+    for (int i = 0; i < n; ++i) g_marks.ev[i] = static_cast<hipEvent_t>(events[i]);
+    g_marks.n = n;
+    g_marks.kinds = n > 0 ? kinds : nullptr;
+    g_marks.launched = n > 0 ? launched : nullptr;
+    return K3MOE_OK;
+}
 
 int k3moe_workspace_size(const k3moe_dims* dims, int act_mode, size_t* bytes)
 {

@@ -223,3 +223,23 @@ def test_forward_cached_rejects_bad_arguments_without_touching_the_gpu():
     assert call(k3.Dims(2, E, k, 7168, 2048)) == k3.K3MOE_EWORKSPACE  # 32 pairs fit; the workspace is for T = 1
     z = k3.Dims(0, E, k, 7168, 2048)
     assert call(z) == k3.K3MOE_OK
+
+
+def test_stage_marks_constants_match_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define K3MOE_MAX_MARKS (\d+)", src)
+    assert m and int(m.group(1)) == k3.MAX_MARKS
+    kinds = {int(v): n.lower() for n, v in re.findall(r"#define K3MOE_KERNEL_([A-Z_]+)\s+(\d+)", src)}
+    assert kinds == k3.KERNEL_KINDS
+
+
+def test_stage_marks_validation_without_touching_the_gpu():
+    lib = k3.lib()
+    P = ctypes.c_void_p
+    ev = (P * 2)(P(0x1000), P(0x2000))  # never recorded: only checked for NULL here
+    assert lib.k3moe_set_stage_marks(ev, -1, None, None) == k3.K3MOE_EINVAL
+    assert lib.k3moe_set_stage_marks(ev, k3.MAX_MARKS + 1, None, None) == k3.K3MOE_EINVAL
+    assert lib.k3moe_set_stage_marks(None, 1, None, None) == k3.K3MOE_EINVAL
+    assert lib.k3moe_set_stage_marks((P * 2)(P(0x1000), None), 2, None, None) == k3.K3MOE_EINVAL
+    # switching marks off always succeeds (and leaves none set for later calls)
+    assert lib.k3moe_set_stage_marks(None, 0, None, None) == k3.K3MOE_OK
