@@ -34,11 +34,12 @@ WsLayout ws_layout(int T, int E, int k, int d, int f, int act_mode)
     L.passes = take((8 * (size_t)pass_stride(E) + 8) * sizeof(int32_t));
     {
         const bool i8 = use_router_i8(T, E, k, d);
-        L.rsl_x = take(i8 ? (size_t)6 * T * d : 0);
-        L.rsl_w = take(i8 ? (size_t)6 * E * d : 0);
+        L.rsl_x = take(i8 ? (size_t)kRouterSlices * T * d : 0);
+        L.rsl_w = take(i8 ? (size_t)kRouterSlices * E * d : 0);
         L.rsl_xe = take(i8 ? (size_t)T * sizeof(int) : 0);
         L.rsl_we = take(i8 ? (size_t)E * sizeof(int) : 0);
         L.rsl_wc = take(i8 ? (size_t)E * sizeof(double) : 0);
+        L.rsl_fail = take(i8 ? ((size_t)T + 1) * sizeof(int) : 0);
     }
     L.route_total = off;
     if (act_mode == K3MOE_ACT_FP32) {
@@ -196,16 +197,18 @@ static void enqueue_route(const k3moe_dims* dm, const float* x, const float* w_r
 {
     double* logits = reinterpret_cast<double*>(ws + L.logits);
     const int bias_in_logits = bias_mode == K3MOE_BIAS_LOGITS;
-    TopkCert cert{nullptr, nullptr, x, w_router, dm->d_model, bias_in_logits};
+    TopkCert cert{nullptr, nullptr, x, w_router, dm->d_model, bias_in_logits, nullptr};
     if (use_router_i8(dm->T, dm->E, dm->k, dm->d_model)) {  // x, w_router 16-B aligned: checked above
         int* xe = reinterpret_cast<int*>(ws + L.rsl_xe);
         double* wc = reinterpret_cast<double*>(ws + L.rsl_wc);
+        int* fail = reinterpret_cast<int*>(ws + L.rsl_fail);
         launch_router_i8(dm->T, dm->E, dm->d_model, x, w_router, bias, bias_in_logits,
                          reinterpret_cast<int8_t*>(ws + L.rsl_x), reinterpret_cast<int8_t*>(ws + L.rsl_w), xe,
                          reinterpret_cast<int*>(ws + L.rsl_we), wc, logits,
-                         reinterpret_cast<double*>(ws + L.partials), s);
+                         reinterpret_cast<double*>(ws + L.partials), fail, s);
         cert.xe = xe;
         cert.wc = wc;
+        cert.fail = fail;
     } else {
         launch_router_logits(dm->T, dm->E, dm->d_model, x, w_router, bias, bias_in_logits, logits,
                              reinterpret_cast<double*>(ws + L.partials), s);

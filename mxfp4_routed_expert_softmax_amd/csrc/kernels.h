@@ -20,11 +20,12 @@ struct WsLayout {
     size_t chunk_base;   // int32  [nch][E]          rows of e before chunk c
     size_t active;       // int32  [E + 1]           active experts, count last
     size_t passes;       // int32  [8*pstride + 8]   MXFP4 gate/up: pass lists per XCD
-    size_t rsl_x;        // int8   [6][T][d]         int8 router: slices of x
-    size_t rsl_w;        // int8   [6][E][d]         int8 router: slices of W_r
+    size_t rsl_x;        // int8   [kRouterSlices][T][d]  int8 router: slices of x
+    size_t rsl_w;        // int8   [kRouterSlices][E][d]  int8 router: slices of W_r
     size_t rsl_xe;       // int32  [T]               int8 router: row exponents of x
     size_t rsl_we;       // int32  [E]               int8 router: row exponents of W_r
     size_t rsl_wc;       // double [E]               int8 router: bound factors
+    size_t rsl_fail;     // int32  [1 + T]           int8 router: tokens left uncertified (count, ids)
     size_t route_total;  // bytes the routing calls need (a prefix of the rest)
     size_t h;            // fp32   [T*k][f]          fp32 mode: SwiGLU output
     size_t o;            // fp32   [T*k][d]          fp32 mode: per-pair down
@@ -52,11 +53,12 @@ void launch_router_logits(int T, int E, int d, const float* x, const float* wr,
 // partials and are added in split order.  Below 256 tokens slicing W_r costs
 // more than the fp64 matrix-core router takes.
 constexpr int kRouterI8MinT = 256;
+constexpr int kRouterSlices = 5;  // int8 slices per operand (7 bits each)
 bool use_router_i8(int T, int E, int k, int d);
 int router_i8_splits(int T, int E, int d);
 void launch_router_i8(int T, int E, int d, const float* x, const float* wr, const float* bias, int bias_in_logits,
                       int8_t* xs, int8_t* wsl, int* xe, int* we, double* wc, double* logits, double* partials,
-                      hipStream_t s);
+                      int* fail, hipStream_t s);
 // What the top-k needs to certify int8 logits (xe null: exact fp64 logits)
 struct TopkCert {
     const int* xe;
@@ -65,6 +67,7 @@ struct TopkCert {
     const float* wr;
     int d;
     int bias_in_logits;
+    int* fail;  // [1 + T]: the tokens whose selection was not certified (count first)
 };
 // top-k + weights + per-chunk masks; for T <= 64 also the whole grouping
 // (logits: rewritten for a token whose certification fails)

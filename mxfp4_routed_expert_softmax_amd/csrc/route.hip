@@ -216,33 +216,40 @@ __global__ __launch_bounds__(256) void router_bias_kernel(long n, int E, const f
 // W_r is scaled by 2^-a, a its exponent (max |v| < 2^a), and cut by
 // truncation into kSl signed 7-bit slices, v = 2^a (sum_p V_p 2^-7(p+1) +
 // r 2^-7kSl) with |r| < 1 -- each step exact in fp32.  The logit x.w is then
-// taken as the slice pairs with p + q <= kSl - 1 (21 of the 36), each an int8
-// dot product summed exactly in int32 on the matrix cores, combined in fp64.
+// taken as the slice pairs with p + q <= kSl - 1 (kSl (kSl + 1) / 2 of the
+// kSl^2: 15 of 25 at five slices), each an int8 dot product summed exactly in
+// int32 on the matrix cores, combined in fp64.
 // Against the exact x.w this is off by less than
 //   2^(a_x - 7 kSl) (kSl d 2^a_w + |w|_1)
 // (truncation of x after kSl slices, and for each slice p of x the
 // truncation of w after kSl - p slices).  The fp64 sums add at most
 // (2 d + 128 + 32 S) 2^-53 2^a_x |w|_1 more, S = the K slices: the oracle's
 // sequential sum of d exact products errs by at most (d - 1) 2^-53 2^a_x
-// |w|_1; every slice of ours adds six exact level terms, each at most (l + 1)
+// |w|_1; every slice of ours adds kSl exact level terms, each at most (l + 1)
 // 2^a_x |w|_1 over the slice (truncated slices never exceed the value), so
-// its five roundings err by at most 105 2^-53 times that, and adding the S
-// slice results by at most 21 (S - 1) 2^-53 2^a_x |w|_1.
+// its kSl - 1 roundings err by at most (kSl - 1) kSl (kSl + 1) / 2 2^-53
+// times that (60 at five slices, 105 at six), and adding the S slice results
+// by at most kSl (kSl + 1) / 2 (S - 1) 2^-53 2^a_x |w|_1 (15 or 21 per add).
 // wc[e] holds that bound's factor of 2^a_x for row e; the top-k of each token
 // then checks that every gap among its best k + 1 keys exceeds twice the
-// token's bound, and recomputes the token's logits exactly in fp64 where one
-// does not (ties, near-ties, an all-zero token), so the selection is the
-// exact-arithmetic one in every case.
-constexpr int kSl = 6;           // slices per operand
+// token's bound.  A token that fails (ties, near-ties) goes to a list whose
+// logits router_exact_kernel recomputes in fp64 and topk_fail_kernel
+// selects from; an all-zero token's logits are exact already (0, plus the
+// bias).  Five slices leave the bound at ~5e-7 of logits of unit scale at the
+// 896-expert layer: about one token in 2,000 of random inputs goes to the list.
+constexpr int kSl = kRouterSlices;  // slices per operand
 constexpr int kZeroRow = -100000;  // exponent marker of an all-zero row
 
 // One row per block (x rows first, then W_r rows): its exponent, its slices
 // ([kSl][rows][d] int8) and, for W_r rows, the bound factor.
+// Block 0 also empties the list of uncertified tokens for this call.
 __global__ __launch_bounds__(256) void router_slice_kernel(int T, int E, int d, int nsplit, const float* __restrict__ x,
                                                            const float* __restrict__ wr, int8_t* __restrict__ xs,
                                                            int8_t* __restrict__ wsl, int* __restrict__ xe,
-                                                           int* __restrict__ we, double* __restrict__ wc)
+                                                           int* __restrict__ we, double* __restrict__ wc,
+                                                           int* __restrict__ fail)
 {
+    if (blockIdx.x == 0 && threadIdx.x == 0) fail[0] = 0;
     __shared__ float redm[4];
     __shared__ double redn[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -434,10 +441,10 @@ int router_i8_splits(int T, int E, int d)
 
 void launch_router_i8(int T, int E, int d, const float* x, const float* wr, const float* bias, int bias_in_logits,
                       int8_t* xs, int8_t* wsl, int* xe, int* we, double* wc, double* logits, double* partials,
-                      hipStream_t s)
+                      int* fail, hipStream_t s)
 {
     const int ns = router_i8_splits(T, E, d);
-    router_slice_kernel<<<dim3(T + E), dim3(256), 0, s>>>(T, E, d, ns, x, wr, xs, wsl, xe, we, wc);
+    router_slice_kernel<<<dim3(T + E), dim3(256), 0, s>>>(T, E, d, ns, x, wr, xs, wsl, xe, we, wc, fail);
     const int total = ((E + 63) / 64) * ((T + 63) / 64) * ns;
     router_i8_kernel<<<dim3(8 * ((total + 7) / 8)), dim3(256), 0, s>>>(T, E, d, xs, wsl, xe, we, bias, bias_in_logits,
                                                                        logits, ns, partials);
@@ -512,47 +519,99 @@ __device__ int block_exclusive_scan(int v, int* wave_tot, int* total)
     return excl;
 }
 
-// Logits of one token, exactly as router_rows forms them (fp64 sums of the
-// exact fp32 x fp32 products), one wave per expert row: the fallback of the
-// certified selection.
-__device__ __forceinline__ void exact_logits_row(int E, int d, const float* __restrict__ xrow,
-                                                 const float* __restrict__ wr, const float* __restrict__ bias,
-                                                 int bias_in_logits, double* __restrict__ lrow)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    for (int e = wave; e < E; e += nw) {
-        const float* w = wr + (size_t)e * d;
-        double acc = 0.0;
-        for (int i = lane; i < d; i += 64) acc = fma((double)xrow[i], (double)w[i], acc);
-        for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-        if (lane == 0) lrow[e] = bias_in_logits ? acc + (double)bias[e] : acc;
-    }
-}
-
 // Top-k of one token per block (16 waves): the selection and the weights of
 // token blockIdx.x.  With xe (logits from the int8 slices): the selection is
-// certified against the token's bound 2^a_x max_e wc[e], and a token that
-// fails gets its logits recomputed exactly (written back) and selected again.
-__global__ __launch_bounds__(1024) void topk_token_kernel(int E, int k, double* __restrict__ logits,
+// certified against the token's bound 2^a_x max_e wc[e]; a token that fails
+// is appended to the fail list (its selection follows in topk_fail_kernel,
+// from logits that router_exact_kernel recomputes).  An all-zero token's
+// logits are exact (0, plus the bias): selected directly.
+__global__ __launch_bounds__(1024) void topk_token_kernel(int E, int k, const double* __restrict__ logits,
                                                           const float* __restrict__ bias, int bias_select_only,
                                                           int sigmoid, int32_t* __restrict__ topk_idx,
                                                           float* __restrict__ topk_w, const int* __restrict__ xe,
-                                                          const double* __restrict__ wc, const float* __restrict__ x,
-                                                          const float* __restrict__ wr, int d, int bias_in_logits)
+                                                          const double* __restrict__ wc, int* __restrict__ fail)
 {
     __shared__ TopkLists lists;
     const int t = blockIdx.x;
-    double* lrow = logits + (size_t)t * E;
+    const double* lrow = logits + (size_t)t * E;
     int32_t* idx = topk_idx + (size_t)t * k;
     float* w = topk_w + (size_t)t * k;
-    if (xe) {
-        const int ax = xe[t];
-        const double xscale = ax == kZeroRow ? 0.0 : ldexp(1.0, ax);
-        if (block_topk_token(E, k, lrow, bias, bias_select_only, sigmoid, lists, nullptr, idx, w, wc, xscale)) return;
-        exact_logits_row(E, d, x + (size_t)t * d, wr, bias, bias_in_logits, lrow);
-        __syncthreads();
+    if (xe && xe[t] != kZeroRow) {
+        const double xscale = ldexp(1.0, xe[t]);
+        if (!block_topk_token(E, k, lrow, bias, bias_select_only, sigmoid, lists, nullptr, idx, w, wc, xscale) &&
+            threadIdx.x == 0)
+            fail[1 + atomicAdd(fail, 1)] = t;
+        return;
     }
     block_topk_token(E, k, lrow, bias, bias_select_only, sigmoid, lists, nullptr, idx, w);
+}
+
+// Exact logits of the tokens on the fail list: block (b, j) forms expert rows
+// 2b and 2b + 1 of list entries j, j + gridDim.y, ... as fp64 sums of the
+// exact fp32 x fp32 products (per thread a strided partial, then a fixed
+// tree: within ~d 2^-53 max|x||w| of the exact dot product, equal rows give
+// equal logits), plus the bias where it belongs in the logits.
+constexpr int kFailSlots = 4;
+
+__global__ __launch_bounds__(256) void router_exact_kernel(int E, int d, const float* __restrict__ x,
+                                                           const float* __restrict__ wr, const float* __restrict__ bias,
+                                                           int bias_in_logits, const int* __restrict__ fail,
+                                                           double* __restrict__ logits)
+{
+    __shared__ double part[2][4];
+    const int n = fail[0];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int e0 = 2 * (int)blockIdx.x, n4 = d >> 2;
+    const float4* w0 = reinterpret_cast<const float4*>(wr + (size_t)e0 * d);
+    const float4* w1 = reinterpret_cast<const float4*>(wr + (size_t)min(e0 + 1, E - 1) * d);
+    for (int j = blockIdx.y; j < n; j += gridDim.y) {
+        const int t = fail[1 + j];
+        const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)t * d);
+        double a0 = 0.0, a1 = 0.0;
+        for (int i = tid; i < n4; i += 256) {
+            const float4 v = x4[i], p = w0[i], q = w1[i];
+            a0 = fma((double)p.x, (double)v.x, a0);
+            a0 = fma((double)p.y, (double)v.y, a0);
+            a0 = fma((double)p.z, (double)v.z, a0);
+            a0 = fma((double)p.w, (double)v.w, a0);
+            a1 = fma((double)q.x, (double)v.x, a1);
+            a1 = fma((double)q.y, (double)v.y, a1);
+            a1 = fma((double)q.z, (double)v.z, a1);
+            a1 = fma((double)q.w, (double)v.w, a1);
+        }
+        for (int m = 32; m >= 1; m >>= 1) {
+            a0 += shfl_xor_d(a0, m);
+            a1 += shfl_xor_d(a1, m);
+        }
+        if (lane == 0) {
+            part[0][wave] = a0;
+            part[1][wave] = a1;
+        }
+        __syncthreads();
+        if (tid < 2 && e0 + tid < E) {
+            double v = ((part[tid][0] + part[tid][1]) + part[tid][2]) + part[tid][3];
+            if (bias_in_logits) v += (double)bias[e0 + tid];
+            logits[(size_t)t * E + e0 + tid] = v;
+        }
+        __syncthreads();  // part is reused by the next entry
+    }
+}
+
+// The selection of the fail-list tokens from their exact logits: block j
+// takes entries j, j + gridDim.x, ...
+__global__ __launch_bounds__(1024) void topk_fail_kernel(int E, int k, const double* __restrict__ logits,
+                                                         const float* __restrict__ bias, int bias_select_only,
+                                                         int sigmoid, int32_t* __restrict__ topk_idx,
+                                                         float* __restrict__ topk_w, const int* __restrict__ fail)
+{
+    __shared__ TopkLists lists;
+    const int n = fail[0];
+    for (int j = blockIdx.x; j < n; j += gridDim.x) {
+        const int t = fail[1 + j];
+        // ends with a block barrier: the lists are free for the next entry
+        block_topk_token(E, k, logits + (size_t)t * E, bias, bias_select_only, sigmoid, lists, nullptr,
+                         topk_idx + (size_t)t * k, topk_w + (size_t)t * k);
+    }
 }
 
 // Grouping, one block per 64-token chunk, 16 waves.  ONE: a single token,
@@ -695,8 +754,13 @@ void launch_topk_group(int T, int E, int k, double* logits, const float* bias,
         return;
     }
     topk_token_kernel<<<dim3(T), dim3(1024), 0, s>>>(E, k, logits, bias, bias_select_only, sigmoid, topk_idx,
-                                                     topk_w, cert.xe, cert.wc, cert.x, cert.wr, cert.d,
-                                                     cert.bias_in_logits);
+                                                     topk_w, cert.xe, cert.wc, cert.fail);
+    if (cert.xe) {
+        router_exact_kernel<<<dim3((E + 1) / 2, kFailSlots), dim3(256), 0, s>>>(E, cert.d, cert.x, cert.wr, bias,
+                                                                               cert.bias_in_logits, cert.fail, logits);
+        topk_fail_kernel<<<dim3(kFailSlots), dim3(1024), 0, s>>>(E, k, logits, bias, bias_select_only, sigmoid,
+                                                                topk_idx, topk_w, cert.fail);
+    }
     topk_group_kernel<false><<<dim3(nch), dim3(1024), 0, s>>>(T, E, k, logits, bias, bias_select_only, sigmoid,
                                                               topk_idx, topk_w, chunk_masks, chunk_base, counts,
                                                               offsets, perm_pair, row_of_pair);

@@ -5,12 +5,12 @@ keeps a top-k only when every gap among the best k + 1 keys exceeds twice a
 per-token bound (else the token is recomputed exactly).  Routing is exact only
 if that bound really covers |our logit - the oracle's logit|.  These tests
 restate the slicing from its definition (each row scaled by 2^-a, a its
-exponent, then cut by truncation into six signed 7-bit slices; the slice
-pairs with p + q <= 5 are kept), evaluate it in rational arithmetic and in the
+exponent, then cut by truncation into NSL = 5 signed 7-bit slices; the
+slice pairs with p + q <= 4 are kept), evaluate it in rational arithmetic and in the
 fp64 order the kernels use, and check against both the exact dot product and
 the oracle's sequential fp64 sum:
 
-    |ours - exact|  <= 2^a_x 2^-42 (6 d 2^a_w + |w|_1)                 (slicing)
+    |ours - exact|  <= 2^a_x 2^-35 (5 d 2^a_w + |w|_1)                 (slicing)
     |ours - oracle| <= that + (2 d + 128 + 32 S) 2^-53 2^a_x |w|_1     (fp64 sums)
 
 on random rows, rows at the top of their binade (largest truncation), rows
@@ -23,7 +23,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-NSL = 6  # slices per operand
+NSL = 5  # slices per operand
 
 
 def _exponent(row):
@@ -35,7 +35,7 @@ def _exponent(row):
 
 
 def _slices(row):
-    """int slices V[p][i] with row = 2^a (sum_p V_p 2^-7(p+1) + r 2^-42)."""
+    """int slices V[p][i] with row = 2^a (sum_p V_p 2^-7(p+1) + r 2^-7NSL)."""
     a = _exponent(row)
     if a is None:
         return None, np.zeros((NSL, row.size), dtype=np.int64)
@@ -50,8 +50,8 @@ def _slices(row):
 
 
 def _ours_fp64(x, w, nsplit):
-    """The kernels' evaluation order: per K slice, six int32 level sums
-    (p + q = l), added in fp64 from l = 5 down, scaled by 2^(a_x + a_w); the
+    """The kernels' evaluation order: per K slice, NSL int32 level sums
+    (p + q = l), added in fp64 from l = NSL - 1 down, scaled by 2^(a_x + a_w); the
     slices' results added in slice order."""
     ax, X = _slices(x)
     aw, W = _slices(w)
@@ -105,7 +105,7 @@ def _bounds(x, w, nsplit):
         return 0.0, 0.0
     d = x.size
     w1 = float(np.sum(np.abs(w.astype(np.float64))))
-    trunc = 2.0 ** ax * 2.0 ** -42 * (NSL * d * 2.0 ** aw + w1)
+    trunc = 2.0 ** ax * 2.0 ** (-7 * NSL) * (NSL * d * 2.0 ** aw + w1)
     rnd = (2 * d + 128 + 32 * nsplit) * 2.0 ** -53 * 2.0 ** ax * w1
     return trunc, rnd
 
@@ -114,7 +114,7 @@ def _rows(kind, d, rng):
     if kind == "normal":
         return rng.standard_normal(d).astype(np.float32), (rng.standard_normal(d) / np.sqrt(d)).astype(np.float32)
     if kind == "top_of_binade":
-        # every entry just below a power of two: the most bits past 42
+        # every entry just below a power of two: the most bits past the slices
         x = (np.float32(np.nextafter(np.float32(2.0), np.float32(0))) *
              rng.choice([-1.0, 1.0], d)).astype(np.float32)
         w = (np.float32(np.nextafter(np.float32(0.125), np.float32(0))) *
@@ -129,7 +129,7 @@ def _rows(kind, d, rng):
         return x, w
     if kind == "aligned_top":
         # same sign everywhere, every mantissa all ones: the dropped slice
-        # pairs (p + q >= 6) all add up instead of cancelling
+        # pairs (p + q >= NSL) all add up instead of cancelling
         x = np.full(d, np.nextafter(np.float32(2.0), np.float32(0)), np.float32)
         w = np.full(d, np.nextafter(np.float32(0.125), np.float32(0)), np.float32)
         return x, w
