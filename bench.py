@@ -313,10 +313,16 @@ def measure(k3, synthdata, torch, dev, wl, experts, wr, steps, warmup, use_graph
             flops = 2.0 * 3 * sh.d * sh.f * T * sh.k
             stage["flops_per_launch"] = flops
             stage["mfma_frac"] = round(flops / (ffn_ms * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS, 4)
-            if dom == "gateup":
-                gflops = 2.0 * 2 * sh.d * sh.f * T * sh.k
-                roofline["flops_per_launch"] = gflops
-                roofline["mfma_frac"] = round(gflops / (kern[dom]["avg_ms"] * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS, 4)
+            kf = {"gateup": 2.0 * 2 * sh.d * sh.f * T * sh.k, "down": 2.0 * sh.d * sh.f * T * sh.k}
+            if dom in kf:
+                tf = kf[dom] / (kern[dom]["avg_ms"] * 1e-3) / 1e12
+                roofline["flops_per_launch"] = kf[dom]
+                roofline["mfma_frac"] = round(tf / MXFP4_PEAK_TFLOPS, 4)
+                # above the ridge (flop per byte over peak flops per peak byte) the matrix peak bounds it
+                if kf[dom] / (MXFP4_PEAK_TFLOPS * 1e12) > kb[dom] / (HBM_PEAK_GBS * 1e9):
+                    roofline.update({"bound": "mfma", "achieved": round(tf, 1), "peak": MXFP4_PEAK_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": roofline["mfma_frac"],
+                                     "hbm_frac": round(achieved / HBM_PEAK_GBS, 4)})
     return dict(fw=fw, xs=xs, nbatch=nbatch, stream=stream, ms_per_step=ms_per_step,
                 tokens_per_s=tokens_per_s, roofline=roofline, n_active=n_active, bias_mode=bias_mode,
                 graph=graph)
