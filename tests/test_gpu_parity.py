@@ -402,8 +402,11 @@ def _limit_layer(name):
 
 # 1024 experts: k = 32 (the largest k; fp64 router at every T), k = 31 and 16
 # at 1100 tokens (the certified int8 router; k = 31 keeps 32 entries per
-# list).  The wide layer: the pair path (T = 1, 3) and the grouped path (T = 70).
-@pytest.mark.parametrize("name,k,T", [("limit_e1024", 32, 1), ("limit_e1024", 32, 70), ("limit_e1024", 32, 1100),
+# list); T = 8 (256 pairs over 1024 experts: the one-token and the
+# several-token gate/up launches of the grouped path side by side).  The
+# wide layer: the pair path (T = 1, 3) and the grouped path (T = 70).
+@pytest.mark.parametrize("name,k,T", [("limit_e1024", 32, 1), ("limit_e1024", 32, 8), ("limit_e1024", 32, 70),
+                                      ("limit_e1024", 32, 1100),
                                       ("limit_e1024", 31, 1100), ("limit_e1024", 16, 1100),
                                       ("wide_d8256", 2, 1), ("wide_d8256", 2, 3), ("wide_d8256", 2, 70)])
 def test_limit_fp32(name, k, T):
