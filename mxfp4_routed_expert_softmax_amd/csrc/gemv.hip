@@ -175,11 +175,15 @@ constexpr int kGuRows = 32;  // row pairs per block
 // scratch traffic cost more than the fourth wave gains).
 // SL (pair path only): h is written as its kSlices MX-FP8 slices (the
 // block's 32 rows are exactly one 32-value block of h) instead of fp32.
-// ONE (grouped, TCH == 1): only the slots whose expert has exactly one token;
-// with the token loop gone it fits 128 registers like the pair form and runs
-// at four waves per SIMD (gateup_gemv_tokens_kernel takes the other slots).
-template <int TCH, int BPL, bool PAIR, bool SL = false, bool ONE = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BPL == 1 && TCH == 1 ? ((PAIR || ONE) ? 4 : 3) : 1, 8)))
+// SEL (grouped path): kSelAll, or only the slots whose expert has exactly one
+// token (kSelOne: with the token loop gone it fits 128 registers like the
+// pair form and runs at four waves per SIMD), or only those with two or more
+// (kSelMulti).
+constexpr int kSelAll = 0, kSelOne = 1, kSelMulti = 2;
+
+template <int TCH, int BPL, bool PAIR, bool SL = false, int SEL = kSelAll>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    BPL == 1 && TCH == 1 ? ((PAIR || SEL == kSelOne) ? 4 : 3) : 1, 8)))
 void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h, uint8_t* __restrict__ hs_codes = nullptr,
                         uint8_t* __restrict__ hs_scales = nullptr)
 {
@@ -193,10 +197,11 @@ void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h, uint8_t* __restrict__ 
     } else if (!slot_expert(a, blockIdx.y, e, r_beg, n_e)) {
         return;
     } else {
-        if (ONE) {
+        if (SEL == kSelOne) {
             if (n_e != 1) return;
             n_e = 1;
         }
+        if (SEL == kSelMulti && n_e < 2) return;
         e = wslot(a, e);
     }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -289,129 +294,6 @@ void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h, uint8_t* __restrict__ 
                 }
                 h[(size_t)(r_beg + t0 + tt) * a.f + r0 + r] = silu_f32(g) * u;
             }
-        }
-        __syncthreads();
-    }
-}
-
-// Grouped gate/up, one token per pass: the weights of a batch are loaded once
-// and applied to every token of the expert (up to kGuTokChunk per weight
-// pass), each token's activation block re-read from L2 per batch, so an
-// expert with n tokens streams its rows from HBM once instead of n times.
-// Per token the sums are formed exactly as in gateup_gemv_kernel<1, BPL,
-// false> (same per-lane order, same reductions): identical results.  Used
-// for d <= 8192 (BPL = 1); two blocks per lane would not fit the registers.
-// Slots with fewer than min_tok tokens are left to another launch.
-constexpr int kGuTokChunk = 8;
-
-template <int BPL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8)))
-void gateup_gemv_tokens_kernel(FfnArgs a, float* __restrict__ h, int min_tok)
-{
-    constexpr int R = 16, HALF = R / 2;
-    __shared__ float part[kGuTokChunk][4][kGuRows * 2];  // [token][wave][gate rows | up rows]
-    int e, r_beg, n_e;
-    if (!slot_expert(a, blockIdx.y, e, r_beg, n_e) || n_e < min_tok) return;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r0 = blockIdx.x * kGuRows;
-    const int d = a.d, nb = d >> 5;
-    const size_t crow = (size_t)(d >> 1), srow = (size_t)nb;
-    const size_t wrow0 = (size_t)wslot(a, e) * a.f + r0;
-    const int npairs = min(kGuRows, a.f - r0);  // multiple of 8 (f % 32 == 0)
-    const __amdgpu_buffer_rsrc_t rg = weight_rsrc(a.gc + wrow0 * crow);
-    const __amdgpu_buffer_rsrc_t ru = weight_rsrc(a.uc + wrow0 * crow);
-    const __amdgpu_buffer_rsrc_t rgs = weight_rsrc(a.gs + wrow0 * srow);
-    const __amdgpu_buffer_rsrc_t rus = weight_rsrc(a.us + wrow0 * srow);
-    uint32_t coff[BPL], soffl[BPL];
-#pragma unroll
-    for (int b = 0; b < BPL; ++b) {
-        const int blk = tid + 256 * b;
-        coff[b] = blk < nb ? (uint32_t)blk * 16u : kOff;
-        soffl[b] = blk < nb ? (uint32_t)blk : kOff;
-    }
-    for (int t0 = 0; t0 < n_e; t0 += kGuTokChunk) {
-        const int nt = min(kGuTokChunk, n_e - t0);
-        for (int pb = 0; pb < npairs; pb += HALF) {
-            uint4 q[R][BPL];
-            uint32_t sb[R][BPL];
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-                const uint32_t row = (uint32_t)(pb + (i % HALF));
-#pragma unroll
-                for (int b = 0; b < BPL; ++b) {
-                    q[i][b] = ld_stream(i < HALF ? rg : ru, coff[b], row * (uint32_t)crow);
-                    sb[i][b] = ld_scale(i < HALF ? rgs : rus, soffl[b], row * (uint32_t)srow);
-                }
-            }
-            float sc[R][BPL];
-#pragma unroll
-            for (int i = 0; i < R; ++i)
-#pragma unroll
-                for (int b = 0; b < BPL; ++b) sc[i][b] = e8m0_f32(sb[i][b]);
-            for (int tt = 0; tt < nt; ++tt) {
-                const int tok = a.perm_pair[r_beg + t0 + tt] / a.k;
-                const float* xrow = a.x + (size_t)tok * d;
-#pragma unroll
-                for (int i = 0; i < R; ++i)
-#pragma unroll
-                    for (int b = 0; b < BPL; ++b) opaque(q[i][b]);  // decode per token, not hoisted out of the loop
-                float acc[16];
-#pragma unroll
-                for (int i = 0; i < R; ++i) acc[i] = 0.f;
-                // per row the products are added in the order of dot32_multi
-                // (block b, then code word k, then the 8 values of the word);
-                // only the loop over rows moved inside, so 8 activation
-                // values are live at a time
-#pragma unroll
-                for (int b = 0; b < BPL; ++b) {
-                    const int blk = tid + 256 * b;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        float x8[8];
-                        if (blk < nb) {
-                            const float4* xp = reinterpret_cast<const float4*>(xrow + (size_t)blk * 32 + 8 * k);
-                            const float4 u0 = xp[0], u1 = xp[1];
-                            x8[0] = u0.x; x8[1] = u0.y; x8[2] = u0.z; x8[3] = u0.w;
-                            x8[4] = u1.x; x8[5] = u1.y; x8[6] = u1.z; x8[7] = u1.w;
-                        } else {
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) x8[j] = 0.f;
-                        }
-#pragma unroll
-                        for (int i = 0; i < R; ++i) {
-                            const uint32_t w = k == 0 ? q[i][b].x : k == 1 ? q[i][b].y : k == 2 ? q[i][b].z : q[i][b].w;
-                            const f32x2 p0 = fp4x2_scaled<0>(w, sc[i][b]);
-                            const f32x2 p1 = fp4x2_scaled<1>(w, sc[i][b]);
-                            const f32x2 p2 = fp4x2_scaled<2>(w, sc[i][b]);
-                            const f32x2 p3 = fp4x2_scaled<3>(w, sc[i][b]);
-                            float t = acc[i];
-                            t = __builtin_fmaf(p0.x, x8[0], t);
-                            t = __builtin_fmaf(p0.y, x8[1], t);
-                            t = __builtin_fmaf(p1.x, x8[2], t);
-                            t = __builtin_fmaf(p1.y, x8[3], t);
-                            t = __builtin_fmaf(p2.x, x8[4], t);
-                            t = __builtin_fmaf(p2.y, x8[5], t);
-                            t = __builtin_fmaf(p3.x, x8[6], t);
-                            t = __builtin_fmaf(p3.y, x8[7], t);
-                            acc[i] = t;
-                        }
-                    }
-                }
-                const float v = wave_transpose_sum16(acc);
-                if (lane < 16) part[tt][wave][lane < HALF ? pb + lane : kGuRows + pb + lane - HALF] = v;
-            }
-        }
-        __syncthreads();
-        // fixed-order cross-wave sum; thread (tt, r) finishes row r of token tt
-        for (int i = tid; i < nt * npairs; i += 256) {
-            const int tt = i / npairs, r = i - tt * npairs;
-            float g = 0.f, u = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                g += part[tt][w][r];
-                u += part[tt][w][kGuRows + r];
-            }
-            h[(size_t)(r_beg + t0 + tt) * a.f + r0 + r] = silu_f32(g) * u;
         }
         __syncthreads();
     }
@@ -664,9 +546,10 @@ __global__ __launch_bounds__(256) void combine_kernel(FfnArgs a, const float* __
 
 // ---------------------------------------------------------------------------
 // Tokens per pass of the grouped GEMVs: one for small batches (about two
-// tokens per active expert: the smaller register set keeps four waves per
-// SIMD and 16 weight rows in flight per wave), two once experts hold many
-// tokens (each decoded weight then serves two activation rows).
+// tokens per active expert; in gate/up the experts with a single token run
+// without the token loop at four waves per SIMD, the others two tokens per
+// pass), two once experts hold many tokens (each decoded weight then serves
+// two activation rows).
 static int tokens_per_pass(const FfnArgs& a) { return a.T <= 64 ? 1 : 2; }
 
 template <int TCH, bool PAIR>
@@ -696,12 +579,12 @@ void launch_gateup_gemv(const FfnArgs& a, float* h, hipStream_t s)
     if (use_pair_path(a)) {
         gateup_dispatch<1, true>(a, h, s);
     } else if (tokens_per_pass(a) == 1 && a.d / 32 <= 256) {
-        // (two blocks per lane do not fit its registers: wider d keeps the token-outer form)
-        // experts with one token at four waves per SIMD, then the others (about half of
-        // each at 64 tokens of uniform routing): 2.23 -> 2.17 ms at 64 tokens
+        // experts with one token at four waves per SIMD, then the others two tokens
+        // per pass, each decoded weight serving both (about half of the active
+        // experts each at 64 tokens of uniform routing)
         const dim3 grid((a.f + kGuRows - 1) / kGuRows, a.nslots);
-        gateup_gemv_kernel<1, 1, false, false, true><<<grid, dim3(256), 0, s>>>(a, h);
-        gateup_gemv_tokens_kernel<1><<<grid, dim3(256), 0, s>>>(a, h, 2);
+        gateup_gemv_kernel<1, 1, false, false, kSelOne><<<grid, dim3(256), 0, s>>>(a, h);
+        gateup_gemv_kernel<2, 1, false, false, kSelMulti><<<grid, dim3(256), 0, s>>>(a, h);
     } else if (tokens_per_pass(a) == 1) {
         gateup_dispatch<1, false>(a, h, s);
     } else
