@@ -178,12 +178,13 @@ constexpr int kGuRows = 32;  // row pairs per block
 // SEL (grouped path): kSelAll, or only the slots whose expert has exactly one
 // token (kSelOne: with the token loop gone it fits 128 registers like the
 // pair form and runs at four waves per SIMD), or only those with two or more
-// (kSelMulti).
+// (kSelMulti, two tokens per pass: four waves per SIMD with two registers
+// spilled outside the row loop, 2.08 -> 2.03 ms at 64 tokens against three).
 constexpr int kSelAll = 0, kSelOne = 1, kSelMulti = 2;
 
 template <int TCH, int BPL, bool PAIR, bool SL = false, int SEL = kSelAll>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
-    BPL == 1 && TCH == 1 ? ((PAIR || SEL == kSelOne) ? 4 : 3) : 1, 8)))
+    BPL == 1 && TCH == 1 ? ((PAIR || SEL == kSelOne) ? 4 : 3) : (SEL == kSelMulti ? 4 : 1), 8)))
 void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h, uint8_t* __restrict__ hs_codes = nullptr,
                         uint8_t* __restrict__ hs_scales = nullptr)
 {
