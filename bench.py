@@ -9,10 +9,10 @@ step (1000 distinct tokens, cycled).
 Prints one JSON line: throughput in tokens/s; the roofline of the dominant
 kernel (its algorithmic bytes -- the active experts' weights it streams, the
 activations it reads, the outputs it writes -- over its average time, taken
-from HIP events that the library records on the launch stream after each
-kernel of the expert-FFN stage), with every kernel of the stage and the whole
-stage (timed by events around k3moe_ffn) beside it; and the fp64 oracle timed
-on the host cores on a bounded sample of the same workload.
+from HIP events attached to each kernel dispatch of the expert-FFN stage on
+the launch stream), with every kernel of the stage and the whole stage
+(timed by events around k3moe_ffn) beside it; and the fp64 oracle timed on
+the host cores on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -206,10 +206,9 @@ def measure(k3, synthdata, torch, dev, wl, experts, wr, steps, warmup, use_graph
             fw.run_ffn()
             ev[1].record(stream)
         else:
-            # the same, with a mark event after every kernel of the stage
+            # the same, every kernel of the stage timed by its own dispatch events
             fw.run_route()
-            mk[0].record(stream)
-            mk[1].set()
+            mk.set()
             try:
                 fw.run_ffn()
             finally:
@@ -239,15 +238,15 @@ def measure(k3, synthdata, torch, dev, wl, experts, wr, steps, warmup, use_graph
     # expert-FFN stage.  An event record costs a few microseconds of stream
     # time, so one-token steps (~0.1 ms) are marked one in EV_EVERY_DECODE
     # (more often when there are fewer than MIN_EV_SAMPLES * EV_EVERY_DECODE).
-    # Kernel marks (k3moe_set_stage_marks) go on other steps than the stage
-    # events when steps are short (their records would lengthen the stage),
-    # on the same steps otherwise.
+    # Kernel marks (k3moe_set_stage_marks: each kernel of the stage launched
+    # with its own start / end events) go on other steps than the stage
+    # events when steps are short, on the same steps otherwise.
     ev_every = max(1, min(EV_EVERY_DECODE if T == 1 else 1, steps // MIN_EV_SAMPLES))
     nev = (steps + ev_every - 1) // ev_every
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
     mk_off = ev_every // 2 if ev_every > 1 else 0
     nmk = len(range(mk_off, steps, ev_every)) if graph is None else 0
-    mks = [(torch.cuda.Event(enable_timing=True), k3.StageMarks(k3.MAX_MARKS, stream)) for _ in range(nmk)]
+    mks = [k3.StageMarks(k3.MAX_MARKS, stream) for _ in range(nmk)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     if graph is None:
@@ -258,8 +257,7 @@ def measure(k3, synthdata, torch, dev, wl, experts, wr, steps, warmup, use_graph
                 fw.set_x(xs[i % nbatch])
                 fw.run_route()
                 ev[0].record(stream)
-                mk[0].record(stream)
-                mk[1].set()
+                mk.set()
                 try:
                     fw.run_ffn()
                 finally:
@@ -395,20 +393,22 @@ KERNEL_NAMES = {"active_list": "active_list", "quantize": "quantize_rows", "gate
 
 
 def kernel_times(mks):
-    """Mean time of each kernel of the stage over the marked steps: the
-    interval from the previous mark (the first: from the start event)."""
+    """Mean time of each kind of kernel of the stage over the marked steps
+    (each kernel's own dispatch start to end; kernels of one kind in a step
+    added up)."""
     acc = {}
     kinds = None
-    for start, m in mks:
+    for m in mks:
         ks = m.kinds()
         if kinds is None:
             kinds = ks
         if ks != kinds:
             raise RuntimeError(f"the stage launched different kernels across steps: {kinds} / {ks}")
-        prev = start
+        step = {}
         for i, n in enumerate(ks):
-            acc.setdefault(n, []).append(prev.elapsed_time(m.events[i]))
-            prev = m.events[i]
+            step[n] = step.get(n, 0.0) + m.kernel_ms(i)
+        for n, t in step.items():
+            acc.setdefault(n, []).append(t)
     return {n: {"avg_ms": float(np.mean(v)), "samples": len(v)} for n, v in acc.items()}
 
 

@@ -264,18 +264,17 @@ int k3moe_cache_read(const void *cache_state, int E, int n_slots, int64_t *stats
 
 /* Kernel timing marks, a measurement aid (not part of the method): per host
  * thread, every later expert-FFN stage (k3moe_ffn and the FFN half of
- * k3moe_forward, k3moe_forward_noalloc, k3moe_forward_cached) records
- * events[i] on its stream right after the i-th kernel it launches, for
- * i < n, and writes that kernel's kind (K3MOE_KERNEL_*) to kinds[i] and the
- * number of kernels the stage launched to *launched (kinds and launched are
+ * k3moe_forward, k3moe_forward_noalloc, k3moe_forward_cached) launches its
+ * i-th kernel, for i < n, with events[2i] and events[2i+1] attached to the
+ * dispatch itself (hipExtLaunchKernel): they take that kernel's start and end
+ * time, so their interval is the kernel's own duration, with nothing added
+ * to the stream.  kinds[i] receives the kernel's kind (K3MOE_KERNEL_*) and
+ * *launched the number of kernels the stage launched (kinds and launched are
  * host memory, either may be NULL, and must stay valid while marks are set).
- * With a start event recorded before the call, the interval up to mark i is
- * kernel i's time on the stream.  events are hipEvent_t created by the
- * caller; each record costs a few microseconds of stream time, so leave
- * marks off outside timing runs, and do not set them while capturing a
- * graph.  n == 0 switches marking off.  Errors: K3MOE_EINVAL for n < 0,
- * n > K3MOE_MAX_MARKS or a NULL event (the marks are then unchanged); a
- * failed record makes the FFN call return K3MOE_EHIP. */
+ * events are 2n hipEvent_t created by the caller; do not set marks while
+ * capturing a graph.  n == 0 switches marking off.  Errors: K3MOE_EINVAL for
+ * n < 0, n > K3MOE_MAX_MARKS or a NULL event (the marks are then unchanged);
+ * launch errors surface as K3MOE_EHIP from the FFN call, as without marks. */
 #define K3MOE_MAX_MARKS 8
 #define K3MOE_KERNEL_ACTIVE_LIST  1  /* active experts (and MXFP4 pass lists)   */
 #define K3MOE_KERNEL_QUANTIZE     2  /* MXFP4 activation quantiser               */

@@ -273,25 +273,27 @@ class Forward:
 
 
 class StageMarks:
-    """Timing marks after the kernels of the expert-FFN stage
-    (k3moe_set_stage_marks).  ``set()`` makes this object's n events the
-    marks of this host thread, ``clear()`` switches marking off.  After a
-    marked call, ``events[i]`` follows kernel i, ``kinds()`` names those
-    kernels and ``launched`` is the number the stage launched."""
+    """Kernel timing marks of the expert-FFN stage (k3moe_set_stage_marks).
+    ``set()`` makes this object's n event pairs the marks of this host
+    thread, ``clear()`` switches marking off.  After a marked call,
+    ``kernel_ms(i)`` is kernel i's own duration (its dispatch's start and end
+    events), ``kinds()`` names the kernels and ``launched`` is the number the
+    stage launched."""
 
     def __init__(self, n=MAX_MARKS, stream=None):
         if not 1 <= n <= MAX_MARKS:
             raise ValueError(f"1 <= n <= {MAX_MARKS}")
         st = stream if stream is not None else torch.cuda.current_stream()
-        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        self.n = n
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
         for e in self.events:
             e.record(st)  # the HIP event is created on the first record
-        self._handles = (ctypes.c_void_p * n)(*[e.cuda_event for e in self.events])
+        self._handles = (ctypes.c_void_p * (2 * n))(*[e.cuda_event for e in self.events])
         self._kinds = (ctypes.c_int * n)()
         self._launched = ctypes.c_int(0)
 
     def set(self):
-        rc = _lib().k3moe_set_stage_marks(self._handles, len(self.events), ctypes.cast(self._kinds, ctypes.c_void_p),
+        rc = _lib().k3moe_set_stage_marks(self._handles, self.n, ctypes.cast(self._kinds, ctypes.c_void_p),
                                           ctypes.c_void_p(ctypes.addressof(self._launched)))
         _check(rc, "k3moe_set_stage_marks")
 
@@ -304,7 +306,10 @@ class StageMarks:
         return self._launched.value
 
     def kinds(self):
-        return [KERNEL_KINDS.get(self._kinds[i], "?") for i in range(min(self.launched, len(self.events)))]
+        return [KERNEL_KINDS.get(self._kinds[i], "?") for i in range(min(self.launched, self.n))]
+
+    def kernel_ms(self, i):
+        return self.events[2 * i].elapsed_time(self.events[2 * i + 1])
 
 
 def k3moe_forward(x, w_router, experts, k, bias=None, bias_mode="none", act_mode="fp32", dbg=None,

@@ -10,6 +10,7 @@
 #include <mutex>
 #include "k3moe.h"
 #include "kernels.h"
+#include "launch.h"
 
 namespace k3 {
 
@@ -221,34 +222,22 @@ static void enqueue_route(const k3moe_dims* dm, const float* x, const float* w_r
 }
 
 // Timing marks of the expert-FFN stage (a measurement aid, per host thread):
-// events recorded on the stream right after each kernel the stage launches.
-struct StageMarks {
-    hipEvent_t ev[K3MOE_MAX_MARKS];
-    int n;
-    int* kinds;     // host [n]: the kernel kind before each mark
-    int* launched;  // host: kernels the last stage launched
-};
-static thread_local StageMarks g_marks{};
+// while a stage is enqueued with marks set, every kernel launched through
+// k3_launch times its own dispatch with the next pair of events.
+thread_local StageMarkState k3::g_stage_marks{};
+static_assert(kMaxMarks == K3MOE_MAX_MARKS, "one limit on marked kernels");
 
-struct MarkCursor {
-    int i = 0;
-    hipError_t err = hipSuccess;
-    void operator()(int kind, hipStream_t s)
+struct MarkScope {
+    MarkScope()
     {
-        if (i < g_marks.n) {
-            if (g_marks.kinds) g_marks.kinds[i] = kind;
-            if (err == hipSuccess) err = hipEventRecord(g_marks.ev[i], s);
-        }
-        ++i;
+        g_stage_marks.active = g_stage_marks.n > 0;
+        g_stage_marks.i = 0;
     }
-    int finish()
+    void kind(int k) { g_stage_marks.kind = k; }  // of the kernels launched next
+    ~MarkScope()
     {
-        if (g_marks.launched) *g_marks.launched = i;
-        if (err != hipSuccess) {
-            g_last_hip_error = (int)err;
-            return K3MOE_EHIP;
-        }
-        return K3MOE_OK;
+        if (g_stage_marks.active && g_stage_marks.launched) *g_stage_marks.launched = g_stage_marks.i;
+        g_stage_marks.active = false;
     }
 };
 
@@ -281,7 +270,7 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
     a.pair_w = pair_slot ? pair_slot : topk_idx;
     a.o_stream = (size_t)a.P * a.d * sizeof(float) > ((size_t)128 << 20) ? 1 : 0;
     const bool pair_path = act_mode == K3MOE_ACT_FP32 && use_pair_path(a);
-    MarkCursor mark;
+    MarkScope mark;
     if (pair_path) {
         a.active = nullptr;  // slots are pairs
         a.nslots = a.P;
@@ -294,8 +283,8 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
         const bool mx = act_mode != K3MOE_ACT_FP32;
         int32_t* passes = reinterpret_cast<int32_t*>(ws + L.passes);
         a.pstride = pass_stride(a.E);
+        mark.kind(K3MOE_KERNEL_ACTIVE_LIST);
         launch_active_list(a.E, offsets, active, mx ? mx_tiles_per_pass() : 0, passes, a.pstride, s);
-        mark(K3MOE_KERNEL_ACTIVE_LIST, s);
         a.active = active;
         a.nslots = a.E;
         a.passes = mx ? passes : nullptr;
@@ -306,30 +295,30 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
         if (pair_path && use_slices_path(a)) {
             uint8_t* hsc = reinterpret_cast<uint8_t*>(ws + L.hs_codes);
             uint8_t* hss = reinterpret_cast<uint8_t*>(ws + L.hs_scales);
+            mark.kind(K3MOE_KERNEL_GATEUP);
             launch_gateup_gemv_slices(a, hsc, hss, s);
-            mark(K3MOE_KERNEL_GATEUP, s);
+            mark.kind(K3MOE_KERNEL_DOWN_COMBINE);
             launch_down_slices(a, hsc, hss, y, s);
-            mark(K3MOE_KERNEL_DOWN_COMBINE, s);
         } else if (pair_path) {
+            mark.kind(K3MOE_KERNEL_GATEUP);
             launch_gateup_gemv(a, h, s);
-            mark(K3MOE_KERNEL_GATEUP, s);
+            mark.kind(K3MOE_KERNEL_DOWN_COMBINE);
             launch_down_gather(a, h, y, s);
-            mark(K3MOE_KERNEL_DOWN_COMBINE, s);
         } else {
+            mark.kind(K3MOE_KERNEL_GATEUP);
             launch_gateup_gemv(a, h, s);
-            mark(K3MOE_KERNEL_GATEUP, s);
+            mark.kind(K3MOE_KERNEL_DOWN);
             launch_down_gemv(a, h, o, s);
-            mark(K3MOE_KERNEL_DOWN, s);
+            mark.kind(K3MOE_KERNEL_COMBINE);
             launch_combine(a, o, y, s);
-            mark(K3MOE_KERNEL_COMBINE, s);
         }
     } else {
         uint8_t* xqc = reinterpret_cast<uint8_t*>(ws + L.xq_codes);
         uint8_t* xqs = reinterpret_cast<uint8_t*>(ws + L.xq_scales);
         uint8_t* hqc = reinterpret_cast<uint8_t*>(ws + L.hq_codes);
         uint8_t* hqs = reinterpret_cast<uint8_t*>(ws + L.hq_scales);
+        mark.kind(K3MOE_KERNEL_QUANTIZE);
         launch_quantize_rows((long)a.T * (a.d / 32), x, xqc, xqs, s);
-        mark(K3MOE_KERNEL_QUANTIZE, s);
         hipError_t err = hipSuccess;
         if (dbg && dbg->x_codes && err == hipSuccess)
             err = hipMemcpyAsync(dbg->x_codes, xqc, (size_t)a.T * a.d / 2, hipMemcpyDeviceToDevice, s);
@@ -339,16 +328,16 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
             g_last_hip_error = (int)err;
             return K3MOE_EHIP;
         }
+        mark.kind(K3MOE_KERNEL_GATEUP);
         launch_gateup_mfma(a, xqc, xqs, hqc, hqs, dbg ? dbg->h : nullptr,
                            dbg ? dbg->h_codes : nullptr, dbg ? dbg->h_scales : nullptr, s);
-        mark(K3MOE_KERNEL_GATEUP, s);
         float* o = reinterpret_cast<float*>(ws + L.o);
+        mark.kind(K3MOE_KERNEL_DOWN);
         launch_down_mfma(a, hqc, hqs, o, s);
-        mark(K3MOE_KERNEL_DOWN, s);
+        mark.kind(K3MOE_KERNEL_COMBINE);
         launch_combine(a, o, y, s);
-        mark(K3MOE_KERNEL_COMBINE, s);
     }
-    return mark.finish();
+    return K3MOE_OK;
 }
 
 extern "C" {
@@ -356,12 +345,12 @@ extern "C" {
 int k3moe_set_stage_marks(void* const* events, int n, int* kinds, int* launched)
 {
     if (n < 0 || n > K3MOE_MAX_MARKS || (n > 0 && !events)) return K3MOE_EINVAL;
-    for (int i = 0; i < n; ++i)
+    for (int i = 0; i < 2 * n; ++i)
         if (!events[i]) return K3MOE_EINVAL;
-    for (int i = 0; i < n; ++i) g_marks.ev[i] = static_cast<hipEvent_t>(events[i]);
-    g_marks.n = n;
-    g_marks.kinds = n > 0 ? kinds : nullptr;
-    g_marks.launched = n > 0 ? launched : nullptr;
+    for (int i = 0; i < 2 * n; ++i) g_stage_marks.ev[i] = static_cast<hipEvent_t>(events[i]);
+    g_stage_marks.n = n;
+    g_stage_marks.kinds = n > 0 ? kinds : nullptr;
+    g_stage_marks.launched = n > 0 ? launched : nullptr;
     return K3MOE_OK;
 }
 

@@ -22,6 +22,7 @@
 // across waves through LDS in a fixed order -- deterministic sums.
 #include "device_common.h"
 #include "kernels.h"
+#include "launch.h"
 #include "slices.h"
 
 namespace k3 {
@@ -559,9 +560,9 @@ static void gateup_dispatch(const FfnArgs& a, float* h, hipStream_t s)
     const int nb = a.d / 32;
     dim3 grid((a.f + kGuRows - 1) / kGuRows, PAIR ? a.P : a.nslots);
     if (nb <= 256)
-        gateup_gemv_kernel<TCH, 1, PAIR><<<grid, dim3(256), 0, s>>>(a, h);
+        k3_launch(gateup_gemv_kernel<TCH, 1, PAIR>, grid, dim3(256), s, a, h, static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr));
     else
-        gateup_gemv_kernel<TCH, 2, PAIR><<<grid, dim3(256), 0, s>>>(a, h);  // d <= kMaxDim: wider rows are refused by the ABI
+        k3_launch(gateup_gemv_kernel<TCH, 2, PAIR>, grid, dim3(256), s, a, h, static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr));  // d <= kMaxDim: wider rows are refused by the ABI
 }
 
 bool use_pair_path(const FfnArgs& a) { return a.P <= kPairMajorMax && a.f <= 8192; }
@@ -570,9 +571,9 @@ void launch_gateup_gemv_slices(const FfnArgs& a, uint8_t* hs_codes, uint8_t* hs_
 {
     const dim3 grid(a.f / kGuRows, a.P);
     if (a.d / 32 <= 256)
-        gateup_gemv_kernel<1, 1, true, true><<<grid, dim3(256), 0, s>>>(a, nullptr, hs_codes, hs_scales);
+        k3_launch(gateup_gemv_kernel<1, 1, true, true>, grid, dim3(256), s, a, static_cast<float*>(nullptr), hs_codes, hs_scales);
     else
-        gateup_gemv_kernel<1, 2, true, true><<<grid, dim3(256), 0, s>>>(a, nullptr, hs_codes, hs_scales);
+        k3_launch(gateup_gemv_kernel<1, 2, true, true>, grid, dim3(256), s, a, static_cast<float*>(nullptr), hs_codes, hs_scales);
 }
 
 void launch_gateup_gemv(const FfnArgs& a, float* h, hipStream_t s)
@@ -584,8 +585,8 @@ void launch_gateup_gemv(const FfnArgs& a, float* h, hipStream_t s)
         // per pass, each decoded weight serving both (about half of the active
         // experts each at 64 tokens of uniform routing)
         const dim3 grid((a.f + kGuRows - 1) / kGuRows, a.nslots);
-        gateup_gemv_kernel<1, 1, false, false, kSelOne><<<grid, dim3(256), 0, s>>>(a, h);
-        gateup_gemv_kernel<2, 1, false, false, kSelMulti><<<grid, dim3(256), 0, s>>>(a, h);
+        k3_launch(gateup_gemv_kernel<1, 1, false, false, kSelOne>, grid, dim3(256), s, a, h, static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr));
+        k3_launch(gateup_gemv_kernel<2, 1, false, false, kSelMulti>, grid, dim3(256), s, a, h, static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr));
     } else if (tokens_per_pass(a) == 1) {
         gateup_dispatch<1, false>(a, h, s);
     } else
@@ -598,11 +599,11 @@ static void down_gather_dispatch(const FfnArgs& a, const float* h, float* y, hip
     const int nb = a.f / 32;
     dim3 grid(a.d / RW, a.T);
     if (nb <= 64)
-        down_gather_kernel<RW, 1><<<grid, dim3(64 * kGatherWaves), 0, s>>>(a, h, y);
+        k3_launch(down_gather_kernel<RW, 1>, grid, dim3(64 * kGatherWaves), s, a, h, y);
     else if (nb <= 128)
-        down_gather_kernel<RW, 2><<<grid, dim3(64 * kGatherWaves), 0, s>>>(a, h, y);
+        k3_launch(down_gather_kernel<RW, 2>, grid, dim3(64 * kGatherWaves), s, a, h, y);
     else
-        down_gather_kernel<RW, 4><<<grid, dim3(64 * kGatherWaves), 0, s>>>(a, h, y);
+        k3_launch(down_gather_kernel<RW, 4>, grid, dim3(64 * kGatherWaves), s, a, h, y);
 }
 
 void launch_down_gather(const FfnArgs& a, const float* h, float* y, hipStream_t s)
@@ -621,9 +622,9 @@ static void down_dispatch_nk(const FfnArgs& a, const float* h, float* o, hipStre
     constexpr int TEAMS = 4 / NK;
     dim3 grid((a.d + TEAMS * kDnRows - 1) / (TEAMS * kDnRows), a.nslots);
     if (nb <= 64 * NK)
-        down_gemv_kernel<TCH, NK, 1><<<grid, dim3(256), 0, s>>>(a, h, o);
+        k3_launch(down_gemv_kernel<TCH, NK, 1>, grid, dim3(256), s, a, h, o);
     else
-        down_gemv_kernel<TCH, NK, 2><<<grid, dim3(256), 0, s>>>(a, h, o);  // f <= kMaxDim: wider rows are refused by the ABI
+        k3_launch(down_gemv_kernel<TCH, NK, 2>, grid, dim3(256), s, a, h, o);  // f <= kMaxDim: wider rows are refused by the ABI
 }
 
 template <int TCH>
@@ -649,7 +650,7 @@ void launch_down_gemv(const FfnArgs& a, const float* h, float* o, hipStream_t s)
 void launch_combine(const FfnArgs& a, const float* o, float* y, hipStream_t s)
 {
     dim3 grid(a.T, (a.d / 4 + 255) / 256);
-    combine_kernel<<<grid, dim3(256), 0, s>>>(a, o, y);
+    k3_launch(combine_kernel, grid, dim3(256), s, a, o, y);
 }
 
 }  // namespace k3

@@ -19,6 +19,7 @@
 // bytes of those blocks arrive in one 32-bit word, and step s selects byte s.
 #include "device_common.h"
 #include "kernels.h"
+#include "launch.h"
 
 namespace k3 {
 
@@ -80,8 +81,8 @@ void launch_quantize_rows(long nblocks, const float* v, uint8_t* codes, uint8_t*
                           hipStream_t s)
 {
     long threads = nblocks * 8;
-    quantize_rows_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s>>>(
-        nblocks, v, codes, scales);
+    k3_launch(quantize_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), s, nblocks, v, codes,
+              scales);
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, size_t n4)
@@ -837,11 +838,11 @@ void launch_gateup_mfma(const FfnArgs& a, const uint8_t* xq_codes, const uint8_t
 {
     const int grid = use_mx512(a) ? mx_grid(a, a.f / kGuTile) : xcd_grid(a.nslots, (a.f + kGuTile - 1) / kGuTile);
     if (use_mx512(a))
-        gateup_mx512_kernel<<<dim3(grid), dim3(256), 0, s>>>(a, xq_codes, xq_scales, hq_codes, hq_scales, dbg_h,
-                                                             dbg_hc, dbg_hs);
+        k3_launch(gateup_mx512_kernel, dim3(grid), dim3(256), s, a, xq_codes, xq_scales, hq_codes, hq_scales, dbg_h,
+                  dbg_hc, dbg_hs);
     else
-        gateup_mfma_kernel<<<dim3(grid), dim3(256), 0, s>>>(a, xq_codes, xq_scales, hq_codes, hq_scales, dbg_h,
-                                                            dbg_hc, dbg_hs);
+        k3_launch(gateup_mfma_kernel, dim3(grid), dim3(256), s, a, xq_codes, xq_scales, hq_codes, hq_scales, dbg_h,
+                  dbg_hc, dbg_hs);
 }
 
 void launch_down_mfma(const FfnArgs& a, const uint8_t* hq_codes, const uint8_t* hq_scales, float* o,
@@ -849,9 +850,9 @@ void launch_down_mfma(const FfnArgs& a, const uint8_t* hq_codes, const uint8_t* 
 {
     const int grid = xcd_grid(a.nslots, (a.d + kDnTile - 1) / kDnTile);
     if (use_mx512(a))
-        down_mx512_kernel<<<dim3(grid), dim3(256), 0, s>>>(a, hq_codes, hq_scales, o);
+        k3_launch(down_mx512_kernel, dim3(grid), dim3(256), s, a, hq_codes, hq_scales, o);
     else
-        down_mfma_kernel<<<dim3(grid), dim3(256), 0, s>>>(a, hq_codes, hq_scales, o);
+        k3_launch(down_mfma_kernel, dim3(grid), dim3(256), s, a, hq_codes, hq_scales, o);
 }
 
 }  // namespace k3

@@ -13,6 +13,7 @@
 #include <float.h>
 #include "device_common.h"
 #include "kernels.h"
+#include "launch.h"
 #include "topk.h"
 
 namespace k3 {
@@ -810,7 +811,7 @@ int pass_stride(int E) { return (E + 7) / 8 + 1; }
 void launch_active_list(int E, const int32_t* offsets, int32_t* active, int mt, int32_t* passes, int pstride,
                         hipStream_t s)
 {
-    active_list_kernel<<<dim3(1), dim3(1024), 0, s>>>(E, offsets, active, mt, passes, pstride);
+    k3_launch(active_list_kernel, dim3(1), dim3(1024), s, E, offsets, active, mt, passes, pstride);
 }
 
 }  // namespace k3

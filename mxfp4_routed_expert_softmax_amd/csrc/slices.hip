@@ -22,6 +22,7 @@
 // (bytes 0-15) and 2 + g'/2 (bytes 16-31), while the E8M0 scale of K-block g
 // still comes from lane group g.
 #include "slices.h"
+#include "launch.h"
 
 namespace k3 {
 
@@ -344,9 +345,9 @@ void launch_down_slices(const FfnArgs& a, const uint8_t* hs_codes, const uint8_t
 {
     // 28 rows per block gives exactly one block per CU at d_model 7168
     if (a.d % 28 == 0 && a.d / 28 >= 256)
-        down_slices_staged_kernel<28, 4><<<dim3(a.d / 28, a.T), dim3(512), 0, s>>>(a, hs_codes, hs_scales, y);
+        k3_launch(down_slices_staged_kernel<28, 4>, dim3(a.d / 28, a.T), dim3(512), s, a, hs_codes, hs_scales, y);
     else
-        down_slices_staged_kernel<16, 4><<<dim3(a.d / 16, a.T), dim3(512), 0, s>>>(a, hs_codes, hs_scales, y);
+        k3_launch(down_slices_staged_kernel<16, 4>, dim3(a.d / 16, a.T), dim3(512), s, a, hs_codes, hs_scales, y);
 }
 
 }  // namespace k3

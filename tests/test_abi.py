@@ -236,10 +236,11 @@ def test_stage_marks_constants_match_header():
 def test_stage_marks_validation_without_touching_the_gpu():
     lib = k3.lib()
     P = ctypes.c_void_p
-    ev = (P * 2)(P(0x1000), P(0x2000))  # never recorded: only checked for NULL here
+    ev = (P * 4)(P(0x1000), P(0x2000), P(0x3000), P(0x4000))  # never used: only checked for NULL here
     assert lib.k3moe_set_stage_marks(ev, -1, None, None) == k3.K3MOE_EINVAL
     assert lib.k3moe_set_stage_marks(ev, k3.MAX_MARKS + 1, None, None) == k3.K3MOE_EINVAL
     assert lib.k3moe_set_stage_marks(None, 1, None, None) == k3.K3MOE_EINVAL
-    assert lib.k3moe_set_stage_marks((P * 2)(P(0x1000), None), 2, None, None) == k3.K3MOE_EINVAL
+    # two events per kernel: the end event of kernel 1 missing
+    assert lib.k3moe_set_stage_marks((P * 4)(P(0x1000), P(0x2000), P(0x3000), None), 2, None, None) == k3.K3MOE_EINVAL
     # switching marks off always succeeds (and leaves none set for later calls)
     assert lib.k3moe_set_stage_marks(None, 0, None, None) == k3.K3MOE_OK

@@ -31,27 +31,29 @@ def test_kernel_bytes_of_the_mx_prefill():
     assert kb["combine"] == P * d * 4 + T * d * 4
 
 
-class _Ev:
-    def __init__(self, t):
-        self.t = t
-
-    def elapsed_time(self, other):
-        return other.t - self.t
-
-
 class _Marks:
     def __init__(self, times, kinds):
-        self.events = [_Ev(t) for t in times]
+        self._t = times
         self._k = kinds
 
     def kinds(self):
         return self._k
 
+    def kernel_ms(self, i):
+        return self._t[i]
 
-def test_kernel_times_are_intervals_between_marks():
-    mks = [(_Ev(0.0), _Marks([0.040, 0.065], ["gateup", "down_combine"])),
-           (_Ev(1.0), _Marks([1.050, 1.075], ["gateup", "down_combine"]))]
+
+def test_kernel_times_average_each_kind_over_steps():
+    mks = [_Marks([0.040, 0.025], ["gateup", "down_combine"]),
+           _Marks([0.050, 0.025], ["gateup", "down_combine"])]
     kt = bench.kernel_times(mks)
     assert abs(kt["gateup"]["avg_ms"] - 0.045) < 1e-12
     assert abs(kt["down_combine"]["avg_ms"] - 0.025) < 1e-12
     assert kt["gateup"]["samples"] == 2
+
+
+def test_kernels_of_one_kind_in_a_step_add_up():
+    # the small-batch gate/up runs as two kernels (one-token experts, then the rest)
+    mks = [_Marks([0.8, 1.2, 1.1, 0.01], ["gateup", "gateup", "down", "combine"])]
+    kt = bench.kernel_times(mks)
+    assert abs(kt["gateup"]["avg_ms"] - 2.0) < 1e-12 and kt["gateup"]["samples"] == 1

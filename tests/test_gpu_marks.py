@@ -1,6 +1,7 @@
 """Kernel timing marks of the expert-FFN stage (k3moe_set_stage_marks) on the
-GPU: the marks name the kernels each path launches, in order, their events
-complete in launch order, and marking changes no output bit."""
+GPU: the marks name the kernels each path launches, in order, each kernel's
+start and end events bracket a positive duration and follow launch order, and
+marking changes no output bit."""
 import numpy as np
 import pytest
 import torch
@@ -45,12 +46,10 @@ def test_marks_name_the_stage_kernels(tiny, T, act, kinds):
     torch.cuda.synchronize()
     y0 = fw.y.clone()
     stream = torch.cuda.current_stream()
-    marks = k3.StageMarks(k3.MAX_MARKS)
-    start = torch.cuda.Event(enable_timing=True)
+    marks = k3.StageMarks(k3.MAX_MARKS, stream)
     marks.set()
     try:
         fw.y.fill_(float("nan"))
-        start.record(stream)
         fw.run_ffn()
     finally:
         k3.StageMarks.clear()
@@ -58,9 +57,12 @@ def test_marks_name_the_stage_kernels(tiny, T, act, kinds):
     assert marks.launched == len(kinds)
     assert marks.kinds() == kinds
     assert torch.equal(fw.y, y0), "marking changed the output"
-    # each mark follows the previous one on the stream
-    t = [start.elapsed_time(marks.events[i]) for i in range(len(kinds))]
-    assert all(v >= 0.0 for v in t) and all(b >= a for a, b in zip(t, t[1:])), t
+    # every kernel's own duration is positive; each starts after the previous ended
+    ev = marks.events
+    dur = [marks.kernel_ms(i) for i in range(len(kinds))]
+    gaps = [ev[2 * i - 1].elapsed_time(ev[2 * i]) for i in range(1, len(kinds))]
+    assert all(v > 0.0 for v in dur), dur
+    assert all(g >= 0.0 for g in gaps), gaps
     # cleared: a later call records nothing and leaves the counts alone
     fw.run_ffn()
     torch.cuda.synchronize()
@@ -71,7 +73,7 @@ def test_fewer_marks_than_kernels(tiny):
     sh, dev, wr = tiny
     x = torch.from_numpy(synthdata.tokens(sh, 65)).to(DEV)
     fw = k3.Forward(x, wr, dev, sh.k, act_mode="mxfp4")
-    marks = k3.StageMarks(2)
+    marks = k3.StageMarks(2, torch.cuda.current_stream())
     marks.set()
     try:
         fw()
