@@ -181,8 +181,9 @@ def measure(k3, synthdata, torch, dev, wl, experts, wr, steps, warmup, use_graph
     Every ev_every-th step issues k3moe_route and k3moe_ffn as two calls with
     HIP events on the launch stream around the expert-FFN stage; as many
     other steps (the same steps when every step carries events) have the
-    library record a mark event after each kernel of the stage; the rest
-    issue k3moe_forward.  At least MIN_EV_SAMPLES steps carry events."""
+    library attach start / end events to each kernel dispatch of the stage;
+    the rest issue k3moe_forward.  At least MIN_EV_SAMPLES steps carry
+    events."""
     sh, T = wl.shape, wl.T
     bias = torch.from_numpy(synthdata.zipf_bias(sh)).to(dev) if wl.zipf_bias else None
     bias_mode = "logits" if wl.zipf_bias else "none"
@@ -239,8 +240,9 @@ def measure(k3, synthdata, torch, dev, wl, experts, wr, steps, warmup, use_graph
     # time, so one-token steps (~0.1 ms) are marked one in EV_EVERY_DECODE
     # (more often when there are fewer than MIN_EV_SAMPLES * EV_EVERY_DECODE).
     # Kernel marks (k3moe_set_stage_marks: each kernel of the stage launched
-    # with its own start / end events) go on other steps than the stage
-    # events when steps are short, on the same steps otherwise.
+    # with its own start / end events, which add nothing to the stream) go on
+    # other steps than the stage events when steps are short (so that the
+    # stage interval holds no marked launch), on the same steps otherwise.
     ev_every = max(1, min(EV_EVERY_DECODE if T == 1 else 1, steps // MIN_EV_SAMPLES))
     nev = (steps + ev_every - 1) // ev_every
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
