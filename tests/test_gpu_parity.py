@@ -200,6 +200,31 @@ def test_int8_router_near_tie_at_k_plus_one(partner):
     assert_route_equal(route, ref)
 
 
+def test_k3_int8_router_many_uncertified_tokens():
+    """The 896-expert router at 300 tokens (int8 slices, K split) with 20
+    router rows duplicated: a token whose top 17 holds a duplicated expert has
+    an exact tie there and cannot be certified, which is about a third of
+    the tokens -- far more than the fallback's four block slots, so its
+    kernels loop over the list -- and three all-zero tokens are selected
+    directly.  Routing must match the oracle bit for bit."""
+    sh = synthdata.K3
+    wr = synthdata.router_weight(sh)
+    rng = np.random.default_rng(300)
+    src = rng.choice(sh.E, 20, replace=False)
+    dst = rng.choice(np.setdiff1d(np.arange(sh.E), src), 20, replace=False)
+    wr[dst] = wr[src]
+    T = 300
+    x = synthdata.tokens(sh, T, first=9000)
+    x[[0, 150, 299]] = 0.0
+    _log("k3 int8 router, 20 duplicated rows, T=300")
+    route = k3.k3moe_route(torch.from_numpy(x).to(DEV), torch.from_numpy(wr).to(DEV), sh.k)
+    torch.cuda.synchronize()
+    ref = oracle.route(x, wr, sh.k)
+    tied = sum(bool(set(r) & set(dst.tolist()) or set(r) & set(src.tolist())) for r in ref["topk_idx"])
+    assert tied >= 40, tied  # the list is long
+    assert_route_equal(route, ref)
+
+
 def _graph_replays_match_eager(xs, wr_dev, experts, k, act="fp32"):
     """k3moe_forward captured once in a HIP graph, then replayed for each
     input in xs (copied into the captured input buffer), with an eager call
