@@ -23,38 +23,8 @@
 
 namespace k3 {
 
-// ---------------------------------------------------------------------------
-// MX quantiser (OCP MX rule): scale byte = clamp(floor(log2 amax) - 2 + 127,
-// 0, 254), 0 for an all-zero block; |v| / 2^(byte-127) rounded to the nearest
-// E2M1 magnitude, ties to the even code, saturating at 6; sign bit kept.
-// Every step is exact in fp32.
-__device__ __forceinline__ uint32_t mx_scale_byte(float amax)
-{
-    if (!(amax > 0.0f)) return 0u;
-    uint32_t b = __float_as_uint(amax);
-    uint32_t ef = b >> 23;
-    int fl = ef ? (int)ef - 127 : (31 - __clz((int)b)) - 149;  // floor(log2 amax)
-    int byte = fl - 2 + 127;
-    return (uint32_t)min(max(byte, 0), 254);
-}
-
-// 2^(127 - byte); byte <= 252 for any finite fp32 amax, so this is normal.
-__device__ __forceinline__ float mx_inv_scale(uint32_t byte)
-{
-    return __uint_as_float((254u - byte) << 23);
-}
-
-__device__ __forceinline__ uint32_t e2m1_encode(float v, float inv_scale)
-{
-    float m = fabsf(v) * inv_scale;
-    // midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5: a tie moves up only when the
-    // upper neighbour has the even code
-    uint32_t idx = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) +
-                   (m > 2.5f) + (m >= 3.5f) + (m > 5.0f);
-    return ((__float_as_uint(v) >> 31) << 3) | idx;
-}
-
-// 8 lanes per 32-element block, 4 values per lane.
+// Activation quantiser (the OCP MX rule of device_common.h): 8 lanes per
+// 32-element block, 4 values per lane.
 __global__ __launch_bounds__(256) void quantize_rows_kernel(long nblocks, const float* __restrict__ v,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales)
@@ -99,7 +69,8 @@ void launch_zero(float* y, size_t n, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
-// Slot -> expert (same rule as the fp32 path).
+// Slot -> expert (same rule as the fp32 path); false as well for the light
+// experts that the GEMVs take (at most a.mx_light tokens).
 __device__ __forceinline__ bool mx_slot_expert(const FfnArgs& a, int slot, int& e, int& r_beg, int& n_e)
 {
     if (a.active) {
@@ -112,7 +83,7 @@ __device__ __forceinline__ bool mx_slot_expert(const FfnArgs& a, int slot, int& 
     }
     r_beg = a.offsets[e];
     n_e = a.offsets[e + 1] - r_beg;
-    return n_e > 0;
+    return n_e > a.mx_light;  // mx_light >= 0
 }
 
 __device__ __forceinline__ i32x8 op4(uint4 q)
@@ -751,15 +722,16 @@ __device__ __forceinline__ void down_mx_item(const FfnArgs& a, int e, int r_beg,
 
 // Work of one gate/up block.  Without pass lists: the (slot, tile) of
 // xcd_tile and all of the slot's passes.  With them, every (slot, tile,
-// pass) is an item: the items of XCD x are its slots x + 8j in order, each
-// as tiles x passes with the passes innermost, so the passes of one (slot,
+// pass) is an item: the items of XCD x are its slots (pslot: the heaviest
+// first, balanced over the XCDs) in order, each as tiles x passes with the
+// passes innermost, so the passes of one (slot,
 // tile) -- the same weight rows, streamed for different tokens -- run side
 // by side on one XCD and share its L2; a heavy expert's passes no longer run
 // one after another in a single block.  Block b takes its XCD's items b/8,
 // b/8 + cap, ... (cap = the grid's blocks per XCD, sized from an estimate of
 // the count).  The down GEMM keeps one block per (slot, tile): its items are
 // a quarter as long (K = d_ff), and per-pass items measured slower there.
-constexpr int kMaxPassList = 1024 / kXcds + 8;
+constexpr int kMaxPassList = 1024 / kXcds + 10;  // pass_stride(1024) + 1 entries
 
 template <typename Body>
 __device__ __forceinline__ void mx_items(const FfnArgs& a, int ntiles, int* scum, Body body)
@@ -789,7 +761,7 @@ __device__ __forceinline__ void mx_items(const FfnArgs& a, int ntiles, int* scum
         const int npass = scum[lo + 1] - scum[lo], r = pos - scum[lo] * ntiles;
         const int tile = r / npass, pass = r - tile * npass;
         int e, r_beg, n_e;
-        mx_slot_expert(a, x + kXcds * lo, e, r_beg, n_e);  // an active slot
+        mx_slot_expert(a, a.pslot[x * a.pstride + lo], e, r_beg, n_e);  // an active slot with passes
         __syncthreads();  // the previous item is done with the LDS
         body(e, r_beg, n_e, tile, pass, pass + 1);
     }
@@ -814,7 +786,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ __attribute__((aligned(16))) uint8_t lds[kMxLds];
     __shared__ uint32_t rowtok[16 * kPassMT];
     int slot, tile, e, r_beg, n_e;
-    if (!xcd_tile(blockIdx.x, a.nslots, a.d / kDnTile, slot, tile)) return;
+    if (a.pslot) {
+        // the gate/up GEMM's balanced slot lists: XCD x takes the d tiles of
+        // its slots, heaviest first (a slot's passes run in one block here)
+        const int x = blockIdx.x % kXcds, pos = blockIdx.x / kXcds, nt = a.d / kDnTile;
+        if (pos / nt >= a.passes[kXcds * a.pstride + x]) return;
+        slot = a.pslot[x * a.pstride + pos / nt];
+        tile = pos % nt;
+    } else if (!xcd_tile(blockIdx.x, a.nslots, a.d / kDnTile, slot, tile)) {
+        return;
+    }
     if (!mx_slot_expert(a, slot, e, r_beg, n_e)) return;
     const int tiles = (n_e + 15) >> 4;
     down_mx_item(a, e, r_beg, n_e, tile, 0, (tiles + kPassMT - 1) / kPassMT, lds, rowtok, hqc, hqs, o);
@@ -848,7 +829,9 @@ void launch_gateup_mfma(const FfnArgs& a, const uint8_t* xq_codes, const uint8_t
 void launch_down_mfma(const FfnArgs& a, const uint8_t* hq_codes, const uint8_t* hq_scales, float* o,
                       hipStream_t s)
 {
-    const int grid = xcd_grid(a.nslots, (a.d + kDnTile - 1) / kDnTile);
+    // with the balanced slot lists an XCD takes up to pstride - 1 slots
+    const int grid = use_mx512(a) && a.pslot ? kXcds * (a.pstride - 1) * (a.d / kDnTile)
+                                             : xcd_grid(a.nslots, (a.d + kDnTile - 1) / kDnTile);
     if (use_mx512(a))
         k3_launch(down_mx512_kernel, dim3(grid), dim3(256), s, a, hq_codes, hq_scales, o);
     else

@@ -575,6 +575,25 @@ def test_k3_batch_t64(k3layer):
     assert_y_close(y, oracle_y_major(x, ref, range(64), sh))
 
 
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_k3_mx_light_dispatch(k3layer, T):
+    """MXFP4 mode at small batches: experts with one or two tokens take the
+    GEMVs on the quantised activations, heavier ones the matrix-core GEMM
+    (T = 1 and 8: almost every expert is light; T = 64: both kinds in one
+    call).  x_q and h_q on every pair, h and y on every token."""
+    sh = k3layer["shape"]
+    x = synthdata.tokens(sh, T, first=30000 + T)
+    dbg = _dbg_buffers(T, sh.k, sh.d, sh.f)
+    y, route = _run(x, k3layer["wr_dev"], k3layer["dev"], sh.k, act="mxfp4", dbg=dbg)
+    ref = oracle.route(x, k3layer["wr"], sh.k)
+    assert_route_equal(route, ref)
+    c = ref["counts"]
+    _log(f"k3 mx T={T}: {int(((c > 0) & (c <= 2)).sum())} light experts, {int((c > 2).sum())} heavy")
+    if T == 64:
+        assert ((c > 0) & (c <= 2)).any() and (c > 2).any(), "the batch should mix light and heavy experts"
+    _check_mx_split(x, ref, dbg, y, range(T), sh.k, shape=sh)
+
+
 def test_k3_prefill_t4096_mx(k3layer):
     """4096-token prefill, MXFP4 activations: routing on every token, x_q and
     h_q on every pair, h and y on >= 128 tokens that give every active expert
