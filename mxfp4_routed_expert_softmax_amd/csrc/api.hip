@@ -336,9 +336,10 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
             return K3MOE_EHIP;
         }
         // tokens-per-expert dispatch: light experts on the GEMVs, the rest on
-        // the matrix-core GEMMs (which skip the light ones); an expert holds
-        // at most T tokens, so with T <= mx_light every expert is light
-        const bool gemm = a.T > a.mx_light;
+        // the matrix-core GEMMs (which skip the ones the GEMVs take); an expert
+        // holds at most T tokens, so with segment heads (no active list) and
+        // T <= mx_light every expert is light and the GEMMs have nothing to do
+        const bool gemm = a.T > a.mx_light || a.active != nullptr;
         const MxIo io{xqc, xqs, hqc, hqs, dbg ? dbg->h : nullptr, dbg ? dbg->h_codes : nullptr,
                       dbg ? dbg->h_scales : nullptr};
         mark.kind(K3MOE_KERNEL_GATEUP);

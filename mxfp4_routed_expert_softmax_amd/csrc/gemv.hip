@@ -775,16 +775,17 @@ void launch_down_gemv(const FfnArgs& a, const float* h, float* o, hipStream_t s)
 bool use_mx_light(const FfnArgs& a) { return a.d / 32 <= 256; }  // one MX block of x per lane
 
 // Blocks per column of the light-expert GEMVs when they walk a light list
-// (each block takes every kLightGrid-th light expert)
-constexpr int kLightGrid = 64;
+// (each block takes every kLightGrid-th light expert; the list may be empty)
+constexpr int kLightGrid = 32;
 
 void launch_gateup_gemv_mx(const FfnArgs& a, const MxIo& io, hipStream_t s)
 {
     const dim3 grid(a.f / kGuRows, a.light_list ? std::min(a.nslots, kLightGrid) : a.nslots);
-    k3_launch(gateup_gemv_kernel<1, 1, false, false, kSelOne, true>, grid, dim3(256), s, a,
-              static_cast<float*>(nullptr), static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr), io);
-    if (a.T > 1 && a.mx_light > 1)  // an expert holds at most T tokens
-        k3_launch(gateup_gemv_kernel<2, 1, false, false, kSelMulti, true>, grid, dim3(256), s, a,
+    if (a.T == 1)  // every expert has one token
+        k3_launch(gateup_gemv_kernel<1, 1, false, false, kSelOne, true>, grid, dim3(256), s, a,
+                  static_cast<float*>(nullptr), static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr), io);
+    else  // one and two tokens alike, two token rows per pass (a lone token's second row is discarded)
+        k3_launch(gateup_gemv_kernel<2, 1, false, false, kSelAll, true>, grid, dim3(256), s, a,
                   static_cast<float*>(nullptr), static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr), io);
 }
 

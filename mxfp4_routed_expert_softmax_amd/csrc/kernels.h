@@ -178,6 +178,11 @@ void launch_down_mfma(const FfnArgs& a, const uint8_t* hq_codes, const uint8_t* 
 // GEMVs below (their matrix tiles would be mostly empty rows), the others the
 // GEMMs above, which skip them; use_mx_light: the GEMV covers these dimensions.
 constexpr int kMxLight = 2;
+// With an active list (more pairs than experts) the GEMVs take the light
+// experts only when there are at least this many (each is 64 gate/up blocks:
+// fewer leave the chip idle during the GEMV launch, and inside the GEMMs they
+// cost less); otherwise the GEMMs take every expert.
+constexpr int kMinLightList = 64;
 bool use_mx_light(const FfnArgs& a);
 void launch_gateup_gemv_mx(const FfnArgs& a, const MxIo& io, hipStream_t s);
 // per-pair rows into o, like launch_down_mfma

@@ -70,7 +70,9 @@ void launch_zero(float* y, size_t n, hipStream_t s)
 
 // ---------------------------------------------------------------------------
 // Slot -> expert (same rule as the fp32 path); false as well for the light
-// experts that the GEMVs take (at most a.mx_light tokens).
+// experts (at most a.mx_light tokens) when the GEMVs take them: always when
+// the slots are segment heads, with an active list when its light list is
+// not empty (active_list_kernel lists all of them or none).
 __device__ __forceinline__ bool mx_slot_expert(const FfnArgs& a, int slot, int& e, int& r_beg, int& n_e)
 {
     if (a.active) {
@@ -83,7 +85,9 @@ __device__ __forceinline__ bool mx_slot_expert(const FfnArgs& a, int slot, int& 
     }
     r_beg = a.offsets[e];
     n_e = a.offsets[e + 1] - r_beg;
-    return n_e > a.mx_light;  // mx_light >= 0
+    if (n_e <= 0) return false;
+    const bool gemv_light = !a.light_list || a.light_list[a.E] > 0;
+    return !(gemv_light && n_e <= a.mx_light);
 }
 
 __device__ __forceinline__ i32x8 op4(uint4 q)
@@ -787,16 +791,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ uint32_t rowtok[16 * kPassMT];
     int slot, tile, e, r_beg, n_e;
     if (a.pslot) {
-        // the gate/up GEMM's balanced slot lists: XCD x takes the d tiles of
-        // its slots, heaviest first (a slot's passes run in one block here)
+        // the gate/up GEMM's balanced slot lists (every slot listed has
+        // passes): XCD x takes the d tiles of its slots, one block running
+        // all of a slot's passes
         const int x = blockIdx.x % kXcds, pos = blockIdx.x / kXcds, nt = a.d / kDnTile;
         if (pos / nt >= a.passes[kXcds * a.pstride + x]) return;
         slot = a.pslot[x * a.pstride + pos / nt];
         tile = pos % nt;
-    } else if (!xcd_tile(blockIdx.x, a.nslots, a.d / kDnTile, slot, tile)) {
+        mx_slot_expert(a, slot, e, r_beg, n_e);
+    } else if (!xcd_tile(blockIdx.x, a.nslots, a.d / kDnTile, slot, tile) || !mx_slot_expert(a, slot, e, r_beg, n_e)) {
         return;
     }
-    if (!mx_slot_expert(a, slot, e, r_beg, n_e)) return;
     const int tiles = (n_e + 15) >> 4;
     down_mx_item(a, e, r_beg, n_e, tile, 0, (tiles + kPassMT - 1) / kPassMT, lds, rowtok, hqc, hqs, o);
 }

@@ -778,8 +778,9 @@ void launch_topk_group(int T, int E, int k, double* logits, const float* bias,
 // Active experts in ascending id (those with at least one token); the count
 // goes to active[E].  With mt > 0 also the MXFP4 pass lists and the list of
 // light experts.  Each active expert needs ceil(tiles / mt) passes of the GEMMs, or
-// none when the GEMVs take it (1 .. light tokens: it goes to light_list,
-// ascending, the count at light_list[E]).  The experts with passes are cut,
+// none when the GEMVs take it (1 .. light tokens, when at least
+// kMinLightList experts are that light: it goes to light_list, ascending, the
+// count at light_list[E]).  The experts with passes are cut,
 // in list order, into eight runs of near-equal total passes (an expert goes
 // to XCD floor(8 * passes before it / all passes)), so each XCD's share is
 // within one expert's passes of an eighth however the load is skewed
@@ -805,8 +806,11 @@ __global__ __launch_bounds__(1024) void active_list_kernel(int E, const int32_t*
     if (flag) active[pos] = e;
     if (e == 0) active[E] = total;
     if (mt <= 0) return;
-    const int is_light = flag && n <= light;
     int nlight;
+    block_exclusive_scan(flag && n <= light, wave_tot, &nlight);
+    // the GEMVs take the light experts only when there are enough of them to
+    // fill the chip; a few (a skewed batch's tail) cost less inside the GEMMs
+    const int is_light = flag && n <= light && nlight >= kMinLightList;
     const int lpos = block_exclusive_scan(is_light, wave_tot, &nlight);
     if (is_light) light_list[lpos] = e;
     if (e == 0) light_list[E] = nlight;

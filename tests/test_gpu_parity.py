@@ -316,7 +316,22 @@ def _check_mx_split(x, ref, dbg, y, tokens, k, get=None, shape=None):
     assert_y_close(y[tokens], y_ref, "y")
 
 
-@pytest.mark.parametrize("T", [1, 37, 300, 1100, 2000])
+@pytest.mark.parametrize("T,k", [(2, 16), (5, 16)])
+def test_tiny_mx_every_expert_light(tiny, T, k):
+    """k = E: every expert holds all T tokens.  T = 2: more pairs than experts
+    (an active list) yet every expert light -- too few of them for the GEMVs,
+    so the matrix-core GEMMs must take them; T = 5: every expert heavy."""
+    sh = tiny["shape"]
+    x = synthdata.tokens(sh, T, first=900 + T)
+    dbg = _dbg_buffers(T, k, sh.d, sh.f)
+    y, route = _run(x, tiny["wr_dev"], tiny["dev"], k, act="mxfp4", dbg=dbg)
+    ref = oracle.route(x, tiny["wr"], k)
+    assert_route_equal(route, ref)
+    assert np.all(ref["counts"] == T)
+    _check_mx_split(x, ref, dbg, y, range(T), k, get=tiny["get"])
+
+
+@pytest.mark.parametrize("T", [1, 2, 37, 300, 1100, 2000])
 def test_tiny_mx_split_step(tiny, T):
     """T = 2000: ~250 tokens per expert, three passes of up to 96 each."""
     sh = tiny["shape"]
