@@ -83,11 +83,7 @@ extern "C" {
 #define K3MOE_ACT_MXFP4  1  /* x quantised per token, h per pair, to MXFP4 (OCP
                                MX rule: scale 2^(floor(log2 amax) - 2), codes
                                round-to-nearest-even, saturating at 6), then
-                               scaled-MXFP4 matrix-core products for experts
-                               with three or more tokens; experts with one or
-                               two take fp32 GEMVs on the decoded x_q / h_q
-                               (d_model <= 8192; the same values, summed in
-                               another order)                               */
+                               scaled-MXFP4 matrix-core products            */
 
 /* ---- shapes ------------------------------------------------------------ */
 typedef struct {

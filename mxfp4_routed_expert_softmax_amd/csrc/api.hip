@@ -31,7 +31,7 @@ WsLayout ws_layout(int T, int E, int k, int d, int f, int act_mode)
     }
     L.chunk_masks = take(nch * E * sizeof(uint64_t));
     L.chunk_base = take(nch * E * sizeof(int32_t));
-    L.active = take(2 * ((size_t)E + 1) * sizeof(int32_t));
+    L.active = take(((size_t)E + 1) * sizeof(int32_t));
     L.passes = take((16 * (size_t)pass_stride(E) + 8) * sizeof(int32_t));
     {
         const bool i8 = use_router_i8(T, E, k, d);
@@ -270,8 +270,6 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
     a.pair_w = pair_slot ? pair_slot : topk_idx;
     a.o_stream = (size_t)a.P * a.d * sizeof(float) > ((size_t)128 << 20) ? 1 : 0;
     const bool pair_path = act_mode == K3MOE_ACT_FP32 && use_pair_path(a);
-    // MXFP4 mode: experts with at most kMxLight tokens take the GEMVs
-    a.mx_light = act_mode == K3MOE_ACT_MXFP4 && use_mx_light(a) ? kMxLight : 0;
     MarkScope mark;
     if (pair_path) {
         a.active = nullptr;  // slots are pairs
@@ -287,14 +285,11 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
         a.pstride = pass_stride(a.E);
         mark.kind(K3MOE_KERNEL_ACTIVE_LIST);
         int32_t* pslot = passes + 8 * a.pstride + 8;
-        int32_t* light_list = active + a.E + 1;
-        launch_active_list(a.E, offsets, active, mx ? mx_tiles_per_pass() : 0, a.mx_light, light_list, passes,
-                           pslot, a.pstride, s);
+        launch_active_list(a.E, offsets, active, mx ? mx_tiles_per_pass() : 0, passes, pslot, a.pstride, s);
         a.active = active;
         a.nslots = a.E;
         a.passes = mx ? passes : nullptr;
         a.pslot = mx ? pslot : nullptr;
-        a.light_list = mx ? light_list : nullptr;
     }
     if (act_mode == K3MOE_ACT_FP32) {
         float* h = reinterpret_cast<float*>(ws + L.h);
@@ -335,20 +330,12 @@ static int enqueue_ffn(const k3moe_dims* dm, const float* x, const k3moe_experts
             g_last_hip_error = (int)err;
             return K3MOE_EHIP;
         }
-        // tokens-per-expert dispatch: light experts on the GEMVs, the rest on
-        // the matrix-core GEMMs (which skip the ones the GEMVs take); an expert
-        // holds at most T tokens, so with segment heads (no active list) and
-        // T <= mx_light every expert is light and the GEMMs have nothing to do
-        const bool gemm = a.T > a.mx_light || a.active != nullptr;
-        const MxIo io{xqc, xqs, hqc, hqs, dbg ? dbg->h : nullptr, dbg ? dbg->h_codes : nullptr,
-                      dbg ? dbg->h_scales : nullptr};
         mark.kind(K3MOE_KERNEL_GATEUP);
-        if (a.mx_light > 0) launch_gateup_gemv_mx(a, io, s);
-        if (gemm) launch_gateup_mfma(a, xqc, xqs, hqc, hqs, io.dbg_h, io.dbg_hc, io.dbg_hs, s);
+        launch_gateup_mfma(a, xqc, xqs, hqc, hqs, dbg ? dbg->h : nullptr,
+                           dbg ? dbg->h_codes : nullptr, dbg ? dbg->h_scales : nullptr, s);
         float* o = reinterpret_cast<float*>(ws + L.o);
         mark.kind(K3MOE_KERNEL_DOWN);
-        if (a.mx_light > 0) launch_down_gemv_mx(a, hqc, hqs, o, s);
-        if (gemm) launch_down_mfma(a, hqc, hqs, o, s);
+        launch_down_mfma(a, hqc, hqs, o, s);
         mark.kind(K3MOE_KERNEL_COMBINE);
         launch_combine(a, o, y, s);
     }

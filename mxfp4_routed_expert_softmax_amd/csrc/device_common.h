@@ -51,36 +51,6 @@ __device__ __forceinline__ void load32f(const float* p, float* xs)
     }
 }
 
-// ---- MX quantiser (OCP MX rule): scale byte = clamp(floor(log2 amax) - 2 + 127,
-// 0, 254), 0 for an all-zero block; |v| / 2^(byte-127) rounded to the nearest
-// E2M1 magnitude, ties to the even code, saturating at 6; sign bit kept.
-// Every step is exact in fp32.
-__device__ __forceinline__ uint32_t mx_scale_byte(float amax)
-{
-    if (!(amax > 0.0f)) return 0u;
-    uint32_t b = __float_as_uint(amax);
-    uint32_t ef = b >> 23;
-    int fl = ef ? (int)ef - 127 : (31 - __clz((int)b)) - 149;  // floor(log2 amax)
-    int byte = fl - 2 + 127;
-    return (uint32_t)min(max(byte, 0), 254);
-}
-
-// 2^(127 - byte); byte <= 252 for any finite fp32 amax, so this is normal.
-__device__ __forceinline__ float mx_inv_scale(uint32_t byte)
-{
-    return __uint_as_float((254u - byte) << 23);
-}
-
-__device__ __forceinline__ uint32_t e2m1_encode(float v, float inv_scale)
-{
-    float m = fabsf(v) * inv_scale;
-    // midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5: a tie moves up only when the
-    // upper neighbour has the even code
-    uint32_t idx = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) +
-                   (m > 2.5f) + (m >= 3.5f) + (m > 5.0f);
-    return ((__float_as_uint(v) >> 31) << 3) | idx;
-}
-
 // ---- buffer loads -------------------------------------------------------
 // Weight rows are read through a buffer resource on the block's (uniform)
 // matrix base: one 32-bit lane offset serves every row (the row offset is a

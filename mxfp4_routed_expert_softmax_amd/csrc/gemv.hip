@@ -20,8 +20,6 @@
 // together, then reduced across the wave with a transposed shuffle
 // reduction (17 swizzles for 16 rows) and, when several waves share a row,
 // across waves through LDS in a fixed order -- deterministic sums.
-#include <algorithm>
-
 #include "device_common.h"
 #include "kernels.h"
 #include "launch.h"
@@ -121,40 +119,6 @@ __device__ __forceinline__ void load_act(const float* row, int blk0, int stride_
     }
 }
 
-// The same slice from an MXFP4 row (codes [nb][16 bytes], scales [nb]),
-// decoded exactly by the scaled convert: the quantised activations of the
-// MXFP4 mode, for experts too light for the matrix-core GEMMs.
-template <int BPL>
-__device__ __forceinline__ void load_act_mx(const uint8_t* codes, const uint8_t* scales, int blk0, int stride_blk,
-                                            int nb, float (&xr)[BPL][32])
-{
-#pragma unroll
-    for (int b = 0; b < BPL; ++b) {
-        const int blk = blk0 + b * stride_blk;
-        if (blk < nb) {
-            const uint4 q = ldg16(codes + 16 * (size_t)blk);
-            const float sc = e8m0_f32(scales[blk]);
-            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const f32x2 p0 = fp4x2_scaled<0>(w[k], sc), p1 = fp4x2_scaled<1>(w[k], sc);
-                const f32x2 p2 = fp4x2_scaled<2>(w[k], sc), p3 = fp4x2_scaled<3>(w[k], sc);
-                xr[b][8 * k + 0] = p0.x;
-                xr[b][8 * k + 1] = p0.y;
-                xr[b][8 * k + 2] = p1.x;
-                xr[b][8 * k + 3] = p1.y;
-                xr[b][8 * k + 4] = p2.x;
-                xr[b][8 * k + 5] = p2.y;
-                xr[b][8 * k + 6] = p3.x;
-                xr[b][8 * k + 7] = p3.y;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) xr[b][i] = 0.f;
-        }
-    }
-}
-
 // Make the compiler treat v as redefined here: stops loop-invariant code
 // motion from hoisting the decode of a weight block out of a token loop
 // (which would keep every decoded value of a batch live at once).
@@ -217,186 +181,123 @@ constexpr int kGuRows = 32;  // row pairs per block
 // pair form and runs at four waves per SIMD), or only those with two or more
 // (kSelMulti, two tokens per pass: four waves per SIMD with two registers
 // spilled outside the row loop, 2.08 -> 2.03 ms at 64 tokens against three).
-// MXA (grouped path, MXFP4 mode): the light experts (FfnArgs::mx_light) on
-// the quantised activations x_q, writing h as MXFP4 rows h_q (the block's 32
-// rows are exactly one 32-value block of h) -- the same OCP quantiser as the
-// matrix-core epilogue; the heavier experts take the matrix-core GEMM.
 constexpr int kSelAll = 0, kSelOne = 1, kSelMulti = 2;
 
-template <int TCH, int BPL, bool PAIR, bool SL = false, int SEL = kSelAll, bool MXA = false>
+template <int TCH, int BPL, bool PAIR, bool SL = false, int SEL = kSelAll>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
-    MXA ? 3 : BPL == 1 && TCH == 1 ? ((PAIR || SEL == kSelOne) ? 4 : 3) : (SEL == kSelMulti ? 4 : 1), 8)))
-void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h, uint8_t* __restrict__ hs_codes,
-                        uint8_t* __restrict__ hs_scales, MxIo mx)
+    BPL == 1 && TCH == 1 ? ((PAIR || SEL == kSelOne) ? 4 : 3) : (SEL == kSelMulti ? 4 : 1), 8)))
+void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h, uint8_t* __restrict__ hs_codes = nullptr,
+                        uint8_t* __restrict__ hs_scales = nullptr)
 {
-    static_assert(!MXA || (!PAIR && !SL), "MXFP4 activations are a grouped-path option");
     constexpr int R = 16 / TCH, HALF = R / 2;
     __shared__ float part[TCH][4][kGuRows * 2];  // [tt][wave][gate rows | up rows]
-    // one slot per block; the MXFP4 light-expert form walks the light list
-    // (a small grid: most slots of a full active list would have no work)
-    for (int slot = blockIdx.y;; slot += gridDim.y) {
-        int e, r_beg, n_e;
-        if (PAIR) {
-            r_beg = blockIdx.y;
-            e = a.pair_w[r_beg];  // weight index (the expert, or its cache slot)
+    int e, r_beg, n_e;
+    if (PAIR) {
+        r_beg = blockIdx.y;
+        e = a.pair_w[r_beg];  // weight index (the expert, or its cache slot)
+        n_e = 1;
+    } else if (!slot_expert(a, blockIdx.y, e, r_beg, n_e)) {
+        return;
+    } else {
+        if (SEL == kSelOne) {
+            if (n_e != 1) return;
             n_e = 1;
-        } else if (MXA && a.light_list) {
-            if (slot >= a.light_list[a.E]) return;
-            e = a.light_list[slot];
-            r_beg = a.offsets[e];
-            n_e = a.offsets[e + 1] - r_beg;
-            if ((SEL == kSelOne && n_e != 1) || (SEL == kSelMulti && n_e < 2)) continue;
-            e = wslot(a, e);
-        } else if (!slot_expert(a, slot, e, r_beg, n_e)) {
-            return;
-        } else {
-            if (SEL == kSelOne) {
-                if (n_e != 1) return;
-                n_e = 1;
-            }
-            if (SEL == kSelMulti && n_e < 2) return;
-            if (MXA && n_e > a.mx_light) return;
-            e = wslot(a, e);
         }
-        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-        const int r0 = blockIdx.x * kGuRows;
-        const int d = a.d, nb = d >> 5;
-        const size_t crow = (size_t)(d >> 1), srow = (size_t)nb;
-        const size_t wrow0 = (size_t)e * a.f + r0;
-        const int npairs = min(kGuRows, a.f - r0);  // multiple of 8 (f % 32 == 0)
-        const __amdgpu_buffer_rsrc_t rg = weight_rsrc(a.gc + wrow0 * crow);
-        const __amdgpu_buffer_rsrc_t ru = weight_rsrc(a.uc + wrow0 * crow);
-        const __amdgpu_buffer_rsrc_t rgs = weight_rsrc(a.gs + wrow0 * srow);
-        const __amdgpu_buffer_rsrc_t rus = weight_rsrc(a.us + wrow0 * srow);
-        uint32_t coff[BPL], soffl[BPL];
-        #pragma unroll
-        for (int b = 0; b < BPL; ++b) {
-            const int blk = tid + 256 * b;
-            coff[b] = blk < nb ? (uint32_t)blk * 16u : kOff;
-            soffl[b] = blk < nb ? (uint32_t)blk : kOff;
-        }
+        if (SEL == kSelMulti && n_e < 2) return;
+        e = wslot(a, e);
+    }
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r0 = blockIdx.x * kGuRows;
+    const int d = a.d, nb = d >> 5;
+    const size_t crow = (size_t)(d >> 1), srow = (size_t)nb;
+    const size_t wrow0 = (size_t)e * a.f + r0;
+    const int npairs = min(kGuRows, a.f - r0);  // multiple of 8 (f % 32 == 0)
+    const __amdgpu_buffer_rsrc_t rg = weight_rsrc(a.gc + wrow0 * crow);
+    const __amdgpu_buffer_rsrc_t ru = weight_rsrc(a.uc + wrow0 * crow);
+    const __amdgpu_buffer_rsrc_t rgs = weight_rsrc(a.gs + wrow0 * srow);
+    const __amdgpu_buffer_rsrc_t rus = weight_rsrc(a.us + wrow0 * srow);
+    uint32_t coff[BPL], soffl[BPL];
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+        const int blk = tid + 256 * b;
+        coff[b] = blk < nb ? (uint32_t)blk * 16u : kOff;
+        soffl[b] = blk < nb ? (uint32_t)blk : kOff;
+    }
 
-        for (int t0 = 0; t0 < n_e; t0 += TCH) {
-            float xr[BPL][TCH][32];
-        #pragma unroll
-            for (int tt = 0; tt < TCH; ++tt) {
-                int m = min(t0 + tt, n_e - 1);
-                int tok = (PAIR ? r_beg : a.perm_pair[r_beg + m]) / a.k;
-                float tmp[BPL][32];
-                if (MXA)
-                    load_act_mx<BPL>(mx.xqc + (size_t)tok * crow, mx.xqs + (size_t)tok * srow, tid, 256, nb, tmp);
-                else
-                    load_act<BPL>(a.x + (size_t)tok * d, tid, 256, nb, tmp);
-        #pragma unroll
-                for (int b = 0; b < BPL; ++b)
-        #pragma unroll
-                    for (int i = 0; i < 32; ++i) xr[b][tt][i] = tmp[b][i];
-            }
-            for (int pb = 0; pb < npairs; pb += HALF) {
-                uint4 q[R][BPL];
-                uint32_t sb[R][BPL];
-        #pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    const uint32_t row = (uint32_t)(pb + (i % HALF));
-        #pragma unroll
-                    for (int b = 0; b < BPL; ++b) {
-                        q[i][b] = ld_stream(i < HALF ? rg : ru, coff[b], row * (uint32_t)crow);
-                        sb[i][b] = ld_scale(i < HALF ? rgs : rus, soffl[b], row * (uint32_t)srow);
-                    }
-                }
-                float acc[16];
-        #pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    float s[TCH];
-        #pragma unroll
-                    for (int tt = 0; tt < TCH; ++tt) s[tt] = 0.f;
-        #pragma unroll
-                    for (int b = 0; b < BPL; ++b) dot32_multi<TCH>(q[i][b], e8m0_f32(sb[i][b]), xr[b], s);
-        #pragma unroll
-                    for (int tt = 0; tt < TCH; ++tt) acc[tt * R + i] = s[tt];
-                }
-                const float v = wave_transpose_sum16(acc);
-                if (lane < 16) {
-                    const int tt = lane / R, i = lane % R;
-                    // gate row pb + i -> slot pb + i; up row pb + i - HALF -> kGuRows + pb + i - HALF
-                    part[tt][wave][i < HALF ? pb + i : kGuRows + pb + i - HALF] = v;
-                }
-            }
-            __syncthreads();
-            if (MXA) {
-                // npairs == 32 (f % 32 == 0): half-wave tt of wave 0 finishes token
-                // t0 + tt's block of h, quantises it (amax by swizzles inside the
-                // half-wave) and packs two codes per byte (element 2i low nibble)
-                if (tid < 64) {
-                    const int tt = tid >> 5, r = tid & 31;
-                    const bool live = tt < TCH && t0 + tt < n_e;
-                    float hv = 0.f;
-                    if (live) {
-                        float g = 0.f, u = 0.f;
-        #pragma unroll
-                        for (int w = 0; w < 4; ++w) {
-                            g += part[tt < TCH ? tt : 0][w][r];
-                            u += part[tt < TCH ? tt : 0][w][kGuRows + r];
-                        }
-                        hv = silu_f32(g) * u;
-                    }
-                    float amax = fabsf(hv);
-                    amax = fmaxf(amax, swz_xor<16>(amax));
-                    amax = fmaxf(amax, swz_xor<8>(amax));
-                    amax = fmaxf(amax, swz_xor<4>(amax));
-                    amax = fmaxf(amax, swz_xor<2>(amax));
-                    amax = fmaxf(amax, swz_xor<1>(amax));
-                    const uint32_t byte = mx_scale_byte(amax);
-                    const uint32_t code = e2m1_encode(hv, mx_inv_scale(byte));
-                    const uint32_t two = code | ((uint32_t)__builtin_amdgcn_ds_swizzle((int)code, (1 << 10) | 0x1F) << 4);
-                    if (live) {
-                        const size_t row = (size_t)(r_beg + t0 + tt), fcb = (size_t)(a.f >> 1), fsb = (size_t)(a.f >> 5);
-                        const size_t cb = (size_t)(r0 >> 1) + (size_t)(r >> 1), blk = (size_t)(r0 >> 5);
-                        if (!(r & 1)) mx.hqc[row * fcb + cb] = (uint8_t)two;
-                        if (r == 0) mx.hqs[row * fsb + blk] = (uint8_t)byte;
-                        if (mx.dbg_h || mx.dbg_hc || mx.dbg_hs) {
-                            const size_t pair = (size_t)a.perm_pair[row];
-                            if (mx.dbg_h) mx.dbg_h[pair * a.f + r0 + r] = hv;
-                            if (mx.dbg_hc && !(r & 1)) mx.dbg_hc[pair * fcb + cb] = (uint8_t)two;
-                            if (mx.dbg_hs && r == 0) mx.dbg_hs[pair * fsb + blk] = (uint8_t)byte;
-                        }
-                    }
-                }
-                __syncthreads();
-                continue;
-            }
-            if (SL) {  // PAIR, TCH == 1, npairs == 32: half-wave 0 holds one MX block of h
-                static_assert(!SL || (PAIR && TCH == 1), "slices output is a pair-path option");
-                if (tid < 32) {
-                    float g = 0.f, u = 0.f;
-        #pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        g += part[0][w][tid];
-                        u += part[0][w][kGuRows + tid];
-                    }
-                    uint32_t code[kSlices], sbyte[kSlices];
-                    split_block(silu_f32(g) * u, code, sbyte);
-                    store_block(tid, r0 >> 5, a.f, hs_codes + (size_t)r_beg * kSlices * a.f,
-                                hs_scales + (size_t)r_beg * kSlices * (a.f >> 5), code, sbyte);
-                }
-                continue;  // one token pass: the loop ends here
-            }
-            // fixed-order cross-wave sum; thread (tt, r) finishes row r of token tt
-            for (int i = tid; i < TCH * npairs; i += 256) {
-                const int tt = i / npairs, r = i - tt * npairs;
-                if (t0 + tt < n_e) {
-                    float g = 0.f, u = 0.f;
-        #pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        g += part[tt][w][r];
-                        u += part[tt][w][kGuRows + r];
-                    }
-                    h[(size_t)(r_beg + t0 + tt) * a.f + r0 + r] = silu_f32(g) * u;
-                }
-            }
-            __syncthreads();
+    for (int t0 = 0; t0 < n_e; t0 += TCH) {
+        float xr[BPL][TCH][32];
+#pragma unroll
+        for (int tt = 0; tt < TCH; ++tt) {
+            int m = min(t0 + tt, n_e - 1);
+            int tok = (PAIR ? r_beg : a.perm_pair[r_beg + m]) / a.k;
+            float tmp[BPL][32];
+            load_act<BPL>(a.x + (size_t)tok * d, tid, 256, nb, tmp);
+#pragma unroll
+            for (int b = 0; b < BPL; ++b)
+#pragma unroll
+                for (int i = 0; i < 32; ++i) xr[b][tt][i] = tmp[b][i];
         }
-        if (!(MXA && a.light_list)) return;
+        for (int pb = 0; pb < npairs; pb += HALF) {
+            uint4 q[R][BPL];
+            uint32_t sb[R][BPL];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const uint32_t row = (uint32_t)(pb + (i % HALF));
+#pragma unroll
+                for (int b = 0; b < BPL; ++b) {
+                    q[i][b] = ld_stream(i < HALF ? rg : ru, coff[b], row * (uint32_t)crow);
+                    sb[i][b] = ld_scale(i < HALF ? rgs : rus, soffl[b], row * (uint32_t)srow);
+                }
+            }
+            float acc[16];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                float s[TCH];
+#pragma unroll
+                for (int tt = 0; tt < TCH; ++tt) s[tt] = 0.f;
+#pragma unroll
+                for (int b = 0; b < BPL; ++b) dot32_multi<TCH>(q[i][b], e8m0_f32(sb[i][b]), xr[b], s);
+#pragma unroll
+                for (int tt = 0; tt < TCH; ++tt) acc[tt * R + i] = s[tt];
+            }
+            const float v = wave_transpose_sum16(acc);
+            if (lane < 16) {
+                const int tt = lane / R, i = lane % R;
+                // gate row pb + i -> slot pb + i; up row pb + i - HALF -> kGuRows + pb + i - HALF
+                part[tt][wave][i < HALF ? pb + i : kGuRows + pb + i - HALF] = v;
+            }
+        }
+        __syncthreads();
+        if (SL) {  // PAIR, TCH == 1, npairs == 32: half-wave 0 holds one MX block of h
+            static_assert(!SL || (PAIR && TCH == 1), "slices output is a pair-path option");
+            if (tid < 32) {
+                float g = 0.f, u = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    g += part[0][w][tid];
+                    u += part[0][w][kGuRows + tid];
+                }
+                uint32_t code[kSlices], sbyte[kSlices];
+                split_block(silu_f32(g) * u, code, sbyte);
+                store_block(tid, r0 >> 5, a.f, hs_codes + (size_t)r_beg * kSlices * a.f,
+                            hs_scales + (size_t)r_beg * kSlices * (a.f >> 5), code, sbyte);
+            }
+            continue;  // one token pass: the loop ends here
+        }
+        // fixed-order cross-wave sum; thread (tt, r) finishes row r of token tt
+        for (int i = tid; i < TCH * npairs; i += 256) {
+            const int tt = i / npairs, r = i - tt * npairs;
+            if (t0 + tt < n_e) {
+                float g = 0.f, u = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    g += part[tt][w][r];
+                    u += part[tt][w][kGuRows + r];
+                }
+                h[(size_t)(r_beg + t0 + tt) * a.f + r0 + r] = silu_f32(g) * u;
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -410,126 +311,107 @@ void gateup_gemv_kernel(FfnArgs a, float* __restrict__ h, uint8_t* __restrict__ 
 // registers: four waves per SIMD without spilling).
 constexpr int kDnRows = 16;  // rows per team
 
-// MXA (MXFP4 mode): the light experts (FfnArgs::mx_light), activations from
-// their h_q rows (hqc [P][f/2], hqs [P][f/32], grouped order) decoded exactly.
-template <int TCH, int NK, int BPL, bool MXA = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
-    TCH == 1 && NK == 1 && BPL == 1 ? (MXA ? 3 : 4) : 1, 8)))
-void down_gemv_kernel(FfnArgs a, const float* __restrict__ hbuf, const uint8_t* __restrict__ hqc,
-                      const uint8_t* __restrict__ hqs, float* __restrict__ o)
+template <int TCH, int NK, int BPL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TCH == 1 && NK == 1 && BPL == 1 ? 4 : 1, 8)))
+void down_gemv_kernel(FfnArgs a, const float* __restrict__ hbuf,
+                                                        float* __restrict__ o)
 {
     constexpr int TEAMS = 4 / NK, R = 16 / TCH;
     __shared__ float part[NK > 1 ? 4 : 1][16];
-    // one slot per block; the MXFP4 light-expert form walks the light list
-    for (int slot = blockIdx.y;; slot += gridDim.y) {
-        int e, r_beg, n_e;
-        if (MXA && a.light_list) {
-            if (slot >= a.light_list[a.E]) return;
-            e = a.light_list[slot];
-            r_beg = a.offsets[e];
-            n_e = a.offsets[e + 1] - r_beg;
-        } else {
-            if (!slot_expert(a, slot, e, r_beg, n_e)) return;
-            if (MXA && n_e > a.mx_light) return;
-        }
-        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-        const int team = wave / NK, kw = wave % NK;
-        const int kl = kw * 64 + lane;  // lane index along the f axis
-        const int c0 = (blockIdx.x * TEAMS + team) * kDnRows;
-        const int f = a.f, nb = f >> 5;
-        const size_t crow = (size_t)(f >> 1), srow = (size_t)nb;
-        const bool live = c0 < a.d;  // d % 16 == 0: a team's rows are all in or all out
-        const size_t wrow0 = (size_t)wslot(a, e) * a.d + (live ? c0 : 0);
-        const __amdgpu_buffer_rsrc_t rd = weight_rsrc(a.dc + wrow0 * crow);
-        const __amdgpu_buffer_rsrc_t rds = weight_rsrc(a.ds + wrow0 * srow);
-        uint32_t coff[BPL], soffl[BPL];
-        #pragma unroll
-        for (int b = 0; b < BPL; ++b) {
-            const int blk = kl + 64 * NK * b;
-            coff[b] = blk < nb ? (uint32_t)blk * 16u : kOff;
-            soffl[b] = blk < nb ? (uint32_t)blk : kOff;
-        }
+    int e, r_beg, n_e;
+    if (!slot_expert(a, blockIdx.y, e, r_beg, n_e)) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int team = wave / NK, kw = wave % NK;
+    const int kl = kw * 64 + lane;  // lane index along the f axis
+    const int c0 = (blockIdx.x * TEAMS + team) * kDnRows;
+    const int f = a.f, nb = f >> 5;
+    const size_t crow = (size_t)(f >> 1), srow = (size_t)nb;
+    const bool live = c0 < a.d;  // d % 16 == 0: a team's rows are all in or all out
+    const size_t wrow0 = (size_t)wslot(a, e) * a.d + (live ? c0 : 0);
+    const __amdgpu_buffer_rsrc_t rd = weight_rsrc(a.dc + wrow0 * crow);
+    const __amdgpu_buffer_rsrc_t rds = weight_rsrc(a.ds + wrow0 * srow);
+    uint32_t coff[BPL], soffl[BPL];
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) {
+        const int blk = kl + 64 * NK * b;
+        coff[b] = blk < nb ? (uint32_t)blk * 16u : kOff;
+        soffl[b] = blk < nb ? (uint32_t)blk : kOff;
+    }
 
-        for (int rb = 0; rb < kDnRows; rb += R) {
-            uint4 q[R][BPL];
-            uint32_t sbp[R / 4][BPL];  // scale bytes four to a register (held across tokens)
-        #pragma unroll
-            for (int b = 0; b < BPL; ++b) {
-                uint32_t sb[R];
-        #pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    q[i][b] = ld_stream(rd, coff[b], (uint32_t)(rb + i) * (uint32_t)crow);
-                    sb[i] = ld_scale(rds, soffl[b], (uint32_t)(rb + i) * (uint32_t)srow);
-                }
-        #pragma unroll
-                for (int j = 0; j < R / 4; ++j)
-                    sbp[j][b] = sb[4 * j] | (sb[4 * j + 1] << 8) | (sb[4 * j + 2] << 16) | (sb[4 * j + 3] << 24);
+    for (int rb = 0; rb < kDnRows; rb += R) {
+        uint4 q[R][BPL];
+        uint32_t sbp[R / 4][BPL];  // scale bytes four to a register (held across tokens)
+#pragma unroll
+        for (int b = 0; b < BPL; ++b) {
+            uint32_t sb[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                q[i][b] = ld_stream(rd, coff[b], (uint32_t)(rb + i) * (uint32_t)crow);
+                sb[i] = ld_scale(rds, soffl[b], (uint32_t)(rb + i) * (uint32_t)srow);
             }
-            for (int t0 = 0; t0 < n_e; t0 += TCH) {
-                float hr[BPL][TCH][32];
-        #pragma unroll
-                for (int tt = 0; tt < TCH; ++tt) {
-                    int m = min(t0 + tt, n_e - 1);
-                    float tmp[BPL][32];
-                    if (MXA)
-                        load_act_mx<BPL>(hqc + (size_t)(r_beg + m) * crow, hqs + (size_t)(r_beg + m) * srow, kl, 64 * NK,
-                                         nb, tmp);
-                    else
-                        load_act<BPL>(hbuf + (size_t)(r_beg + m) * f, kl, 64 * NK, nb, tmp);
-        #pragma unroll
-                    for (int b = 0; b < BPL; ++b)
-        #pragma unroll
-                        for (int i = 0; i < 32; ++i) hr[b][tt][i] = tmp[b][i];
+#pragma unroll
+            for (int j = 0; j < R / 4; ++j)
+                sbp[j][b] = sb[4 * j] | (sb[4 * j + 1] << 8) | (sb[4 * j + 2] << 16) | (sb[4 * j + 3] << 24);
+        }
+        for (int t0 = 0; t0 < n_e; t0 += TCH) {
+            float hr[BPL][TCH][32];
+#pragma unroll
+            for (int tt = 0; tt < TCH; ++tt) {
+                int m = min(t0 + tt, n_e - 1);
+                float tmp[BPL][32];
+                load_act<BPL>(hbuf + (size_t)(r_beg + m) * f, kl, 64 * NK, nb, tmp);
+#pragma unroll
+                for (int b = 0; b < BPL; ++b)
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) hr[b][tt][i] = tmp[b][i];
+            }
+            auto row_dot = [&](int i, float (&s)[TCH]) {
+#pragma unroll
+                for (int tt = 0; tt < TCH; ++tt) s[tt] = 0.f;
+#pragma unroll
+                for (int b = 0; b < BPL; ++b) {
+                    uint4 qq = q[i][b];
+                    uint32_t sp = sbp[i >> 2][b];
+                    opaque(qq);
+                    asm volatile("" : "+v"(sp));
+                    dot32_multi<TCH>(qq, e8m0_f32((sp >> (8 * (i & 3))) & 0xffu), hr[b], s);
                 }
-                auto row_dot = [&](int i, float (&s)[TCH]) {
-        #pragma unroll
-                    for (int tt = 0; tt < TCH; ++tt) s[tt] = 0.f;
-        #pragma unroll
-                    for (int b = 0; b < BPL; ++b) {
-                        uint4 qq = q[i][b];
-                        uint32_t sp = sbp[i >> 2][b];
-                        opaque(qq);
-                        asm volatile("" : "+v"(sp));
-                        dot32_multi<TCH>(qq, e8m0_f32((sp >> (8 * (i & 3))) & 0xffu), hr[b], s);
-                    }
-                };
-                float a8[8];
-        #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    float lo, hi;
-                    if (TCH == 1) {
-                        float s0[TCH], s1[TCH];
-                        row_dot(j, s0);
-                        row_dot(j + 8, s1);
-                        lo = s0[0];
-                        hi = s1[TCH - 1];
-                    } else {
-                        float s2[TCH];
-                        row_dot(j, s2);
-                        lo = s2[0];
-                        hi = s2[TCH - 1];
-                    }
-                    a8[j] = transpose_step8(lo, hi);
-                }
-                const float v = wave_transpose_sum_from8(a8);
-                const int tt = (lane & 15) / R, i = (lane & 15) % R;
-                if (NK == 1) {
-                    if (live && lane < 16 && t0 + tt < n_e)
-                        o[(size_t)(r_beg + t0 + tt) * a.d + c0 + rb + i] = v;
+            };
+            float a8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float lo, hi;
+                if (TCH == 1) {
+                    float s0[TCH], s1[TCH];
+                    row_dot(j, s0);
+                    row_dot(j + 8, s1);
+                    lo = s0[0];
+                    hi = s1[TCH - 1];
                 } else {
-                    if (lane < 16) part[wave][lane] = v;
-                    __syncthreads();
-                    if (kw == 0 && lane < 16 && live && t0 + tt < n_e) {
-                        float sum = 0.f;
-        #pragma unroll
-                        for (int w = 0; w < NK; ++w) sum += part[team * NK + w][lane];
-                        o[(size_t)(r_beg + t0 + tt) * a.d + c0 + rb + i] = sum;
-                    }
-                    __syncthreads();
+                    float s2[TCH];
+                    row_dot(j, s2);
+                    lo = s2[0];
+                    hi = s2[TCH - 1];
                 }
+                a8[j] = transpose_step8(lo, hi);
+            }
+            const float v = wave_transpose_sum_from8(a8);
+            const int tt = (lane & 15) / R, i = (lane & 15) % R;
+            if (NK == 1) {
+                if (live && lane < 16 && t0 + tt < n_e)
+                    o[(size_t)(r_beg + t0 + tt) * a.d + c0 + rb + i] = v;
+            } else {
+                if (lane < 16) part[wave][lane] = v;
+                __syncthreads();
+                if (kw == 0 && lane < 16 && live && t0 + tt < n_e) {
+                    float sum = 0.f;
+#pragma unroll
+                    for (int w = 0; w < NK; ++w) sum += part[team * NK + w][lane];
+                    o[(size_t)(r_beg + t0 + tt) * a.d + c0 + rb + i] = sum;
+                }
+                __syncthreads();
             }
         }
-        if (!(MXA && a.light_list)) return;
     }
 }
 
@@ -678,9 +560,9 @@ static void gateup_dispatch(const FfnArgs& a, float* h, hipStream_t s)
     const int nb = a.d / 32;
     dim3 grid((a.f + kGuRows - 1) / kGuRows, PAIR ? a.P : a.nslots);
     if (nb <= 256)
-        k3_launch(gateup_gemv_kernel<TCH, 1, PAIR>, grid, dim3(256), s, a, h, static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr), MxIo{});
+        k3_launch(gateup_gemv_kernel<TCH, 1, PAIR>, grid, dim3(256), s, a, h, static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr));
     else
-        k3_launch(gateup_gemv_kernel<TCH, 2, PAIR>, grid, dim3(256), s, a, h, static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr), MxIo{});  // d <= kMaxDim: wider rows are refused by the ABI
+        k3_launch(gateup_gemv_kernel<TCH, 2, PAIR>, grid, dim3(256), s, a, h, static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr));  // d <= kMaxDim: wider rows are refused by the ABI
 }
 
 bool use_pair_path(const FfnArgs& a) { return a.P <= kPairMajorMax && a.f <= 8192; }
@@ -689,9 +571,9 @@ void launch_gateup_gemv_slices(const FfnArgs& a, uint8_t* hs_codes, uint8_t* hs_
 {
     const dim3 grid(a.f / kGuRows, a.P);
     if (a.d / 32 <= 256)
-        k3_launch(gateup_gemv_kernel<1, 1, true, true>, grid, dim3(256), s, a, static_cast<float*>(nullptr), hs_codes, hs_scales, MxIo{});
+        k3_launch(gateup_gemv_kernel<1, 1, true, true>, grid, dim3(256), s, a, static_cast<float*>(nullptr), hs_codes, hs_scales);
     else
-        k3_launch(gateup_gemv_kernel<1, 2, true, true>, grid, dim3(256), s, a, static_cast<float*>(nullptr), hs_codes, hs_scales, MxIo{});
+        k3_launch(gateup_gemv_kernel<1, 2, true, true>, grid, dim3(256), s, a, static_cast<float*>(nullptr), hs_codes, hs_scales);
 }
 
 void launch_gateup_gemv(const FfnArgs& a, float* h, hipStream_t s)
@@ -703,8 +585,8 @@ void launch_gateup_gemv(const FfnArgs& a, float* h, hipStream_t s)
         // per pass, each decoded weight serving both (about half of the active
         // experts each at 64 tokens of uniform routing)
         const dim3 grid((a.f + kGuRows - 1) / kGuRows, a.nslots);
-        k3_launch(gateup_gemv_kernel<1, 1, false, false, kSelOne>, grid, dim3(256), s, a, h, static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr), MxIo{});
-        k3_launch(gateup_gemv_kernel<2, 1, false, false, kSelMulti>, grid, dim3(256), s, a, h, static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr), MxIo{});
+        k3_launch(gateup_gemv_kernel<1, 1, false, false, kSelOne>, grid, dim3(256), s, a, h, static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr));
+        k3_launch(gateup_gemv_kernel<2, 1, false, false, kSelMulti>, grid, dim3(256), s, a, h, static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr));
     } else if (tokens_per_pass(a) == 1) {
         gateup_dispatch<1, false>(a, h, s);
     } else
@@ -733,68 +615,36 @@ void launch_down_gather(const FfnArgs& a, const float* h, float* y, hipStream_t 
         down_gather_dispatch<16>(a, h, y, s);
 }
 
-template <int TCH, int NK, bool MXA>
-static void down_dispatch_nk(const FfnArgs& a, const float* h, const uint8_t* hqc, const uint8_t* hqs, float* o,
-                             hipStream_t s)
+template <int TCH, int NK>
+static void down_dispatch_nk(const FfnArgs& a, const float* h, float* o, hipStream_t s)
 {
     const int nb = a.f / 32;
     constexpr int TEAMS = 4 / NK;
     dim3 grid((a.d + TEAMS * kDnRows - 1) / (TEAMS * kDnRows), a.nslots);
     if (nb <= 64 * NK)
-        k3_launch(down_gemv_kernel<TCH, NK, 1, MXA>, grid, dim3(256), s, a, h, hqc, hqs, o);
+        k3_launch(down_gemv_kernel<TCH, NK, 1>, grid, dim3(256), s, a, h, o);
     else
-        k3_launch(down_gemv_kernel<TCH, NK, 2, MXA>, grid, dim3(256), s, a, h, hqc, hqs, o);  // f <= kMaxDim: wider rows are refused by the ABI
+        k3_launch(down_gemv_kernel<TCH, NK, 2>, grid, dim3(256), s, a, h, o);  // f <= kMaxDim: wider rows are refused by the ABI
 }
 
-template <int TCH, bool MXA = false>
-static void down_dispatch(const FfnArgs& a, const float* h, const uint8_t* hqc, const uint8_t* hqs, float* o,
-                          hipStream_t s)
+template <int TCH>
+static void down_dispatch(const FfnArgs& a, const float* h, float* o, hipStream_t s)
 {
     const int nb = a.f / 32;
     if (nb <= 64)
-        down_dispatch_nk<TCH, 1, MXA>(a, h, hqc, hqs, o, s);
+        down_dispatch_nk<TCH, 1>(a, h, o, s);
     else if (nb <= 128)
-        down_dispatch_nk<TCH, 2, MXA>(a, h, hqc, hqs, o, s);
+        down_dispatch_nk<TCH, 2>(a, h, o, s);
     else
-        down_dispatch_nk<TCH, 4, MXA>(a, h, hqc, hqs, o, s);
+        down_dispatch_nk<TCH, 4>(a, h, o, s);
 }
 
 void launch_down_gemv(const FfnArgs& a, const float* h, float* o, hipStream_t s)
 {
     if (tokens_per_pass(a) == 1)
-        down_dispatch<1>(a, h, nullptr, nullptr, o, s);
+        down_dispatch<1>(a, h, o, s);
     else
-        down_dispatch<2>(a, h, nullptr, nullptr, o, s);
-}
-
-// ---------------------------------------------------------------------------
-// MXFP4 mode, experts with 1 .. a.mx_light tokens (the rest take the
-// matrix-core GEMMs, which skip these): a 16-token matrix tile would carry one
-// or two useful rows while streaming the same weight bytes, so these experts
-// take the GEMVs, whose one-token form streams at ~6.6 TB/s.
-bool use_mx_light(const FfnArgs& a) { return a.d / 32 <= 256; }  // one MX block of x per lane
-
-// Blocks per column of the light-expert GEMVs when they walk a light list
-// (each block takes every kLightGrid-th light expert; the list may be empty)
-constexpr int kLightGrid = 32;
-
-void launch_gateup_gemv_mx(const FfnArgs& a, const MxIo& io, hipStream_t s)
-{
-    const dim3 grid(a.f / kGuRows, a.light_list ? std::min(a.nslots, kLightGrid) : a.nslots);
-    if (a.T == 1)  // every expert has one token
-        k3_launch(gateup_gemv_kernel<1, 1, false, false, kSelOne, true>, grid, dim3(256), s, a,
-                  static_cast<float*>(nullptr), static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr), io);
-    else  // one and two tokens alike, two token rows per pass (a lone token's second row is discarded)
-        k3_launch(gateup_gemv_kernel<2, 1, false, false, kSelAll, true>, grid, dim3(256), s, a,
-                  static_cast<float*>(nullptr), static_cast<uint8_t*>(nullptr), static_cast<uint8_t*>(nullptr), io);
-}
-
-void launch_down_gemv_mx(const FfnArgs& a, const uint8_t* hq_codes, const uint8_t* hq_scales, float* o,
-                         hipStream_t s)
-{
-    FfnArgs b = a;
-    if (a.light_list) b.nslots = std::min(a.nslots, kLightGrid);  // the grid's rows; blocks walk the list
-    down_dispatch<1, true>(b, nullptr, hq_codes, hq_scales, o, s);
+        down_dispatch<2>(a, h, o, s);
 }
 
 void launch_combine(const FfnArgs& a, const float* o, float* y, hipStream_t s)

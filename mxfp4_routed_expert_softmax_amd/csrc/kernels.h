@@ -18,7 +18,7 @@ struct WsLayout {
     size_t partials;     // double [nsplit][T][E]    split-K router partial sums
     size_t chunk_masks;  // uint64 [nch][E]          which chunk tokens chose e
     size_t chunk_base;   // int32  [nch][E]          rows of e before chunk c
-    size_t active;       // int32  [2][E + 1]        active experts, then light experts (MXFP4), counts last
+    size_t active;       // int32  [E + 1]           active experts, count last
     size_t passes;       // int32  [16*pstride + 8]  MXFP4 gate/up: pass lists per XCD, then their slots
     size_t rsl_x;        // int8   [kRouterSlices][T][d]  int8 router: slices of x
     size_t rsl_w;        // int8   [kRouterSlices][E][d]  int8 router: slices of W_r
@@ -77,10 +77,9 @@ void launch_topk_group(int T, int E, int k, double* logits, const float* bias,
                        int32_t* offsets, int32_t* perm_pair, int32_t* row_of_pair,
                        const TopkCert& cert, hipStream_t s);
 // active list; with mt > 0 also the per-XCD pass lists of FfnArgs::passes
-// and ::pslot (mt token tiles of 16 per pass) and ::light_list (the experts
-// with at most `light` tokens: they get no passes, the GEMVs take them)
-void launch_active_list(int E, const int32_t* offsets, int32_t* active, int mt, int light, int32_t* light_list,
-                        int32_t* passes, int32_t* pslot, int pstride, hipStream_t s);
+// and ::pslot (mt token tiles of 16 per pass)
+void launch_active_list(int E, const int32_t* offsets, int32_t* active, int mt, int32_t* passes, int32_t* pslot,
+                        int pstride, hipStream_t s);
 int pass_stride(int E);
 int mx_tiles_per_pass();
 
@@ -104,9 +103,6 @@ struct FfnArgs {
     const int32_t* passes;
     const int32_t* pslot;
     int pstride;
-    // MXFP4 GEMVs with an active list: the light experts, ascending, their
-    // count at light_list[E] (null: slots are segment heads)
-    const int32_t* light_list;
     // HBM expert cache: weights of expert e sit at slot slot_of[e] of the
     // weight arrays (null: at e itself)
     const int32_t* slot_of;
@@ -118,22 +114,6 @@ struct FfnArgs {
     // (expert cache) the slot of that pair's expert -- one load, no branch, in
     // kernels that run at the edge of their register budget
     const int32_t* pair_w;
-    // MXFP4 mode: experts with 1 .. mx_light tokens take the GEMVs on the
-    // quantised activations, the others the matrix-core GEMMs (0: all of them
-    // the GEMMs; always 0 in fp32 mode)
-    int mx_light;
-};
-
-// MXFP4-mode GEMV operands: x_q rows (in), h_q rows (out, grouped order) and
-// the optional per-pair copies of h, h_q (k3moe_debug)
-struct MxIo {
-    const uint8_t* xqc;
-    const uint8_t* xqs;
-    uint8_t* hqc;
-    uint8_t* hqs;
-    float* dbg_h;
-    uint8_t* dbg_hc;
-    uint8_t* dbg_hs;
 };
 
 // Index of expert e's weights in the weight arrays
@@ -174,20 +154,6 @@ void launch_zero(float* y, size_t n, hipStream_t s);
 // per-pair rows into o [T*k][d] (grouped order) for launch_combine
 void launch_down_mfma(const FfnArgs& a, const uint8_t* hq_codes, const uint8_t* hq_scales, float* o,
                       hipStream_t s);
-// Tokens-per-expert dispatch: experts with at most kMxLight tokens take the
-// GEMVs below (their matrix tiles would be mostly empty rows), the others the
-// GEMMs above, which skip them; use_mx_light: the GEMV covers these dimensions.
-constexpr int kMxLight = 2;
-// With an active list (more pairs than experts) the GEMVs take the light
-// experts only when there are at least this many (each is 64 gate/up blocks:
-// fewer leave the chip idle during the GEMV launch, and inside the GEMMs they
-// cost less); otherwise the GEMMs take every expert.
-constexpr int kMinLightList = 64;
-bool use_mx_light(const FfnArgs& a);
-void launch_gateup_gemv_mx(const FfnArgs& a, const MxIo& io, hipStream_t s);
-// per-pair rows into o, like launch_down_mfma
-void launch_down_gemv_mx(const FfnArgs& a, const uint8_t* hq_codes, const uint8_t* hq_scales, float* o,
-                         hipStream_t s);
 
 // ---- HBM expert cache (cache.hip) -------------------------------------------
 struct CacheLayout {

@@ -23,8 +23,38 @@
 
 namespace k3 {
 
-// Activation quantiser (the OCP MX rule of device_common.h): 8 lanes per
-// 32-element block, 4 values per lane.
+// ---------------------------------------------------------------------------
+// MX quantiser (OCP MX rule): scale byte = clamp(floor(log2 amax) - 2 + 127,
+// 0, 254), 0 for an all-zero block; |v| / 2^(byte-127) rounded to the nearest
+// E2M1 magnitude, ties to the even code, saturating at 6; sign bit kept.
+// Every step is exact in fp32.
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax)
+{
+    if (!(amax > 0.0f)) return 0u;
+    uint32_t b = __float_as_uint(amax);
+    uint32_t ef = b >> 23;
+    int fl = ef ? (int)ef - 127 : (31 - __clz((int)b)) - 149;  // floor(log2 amax)
+    int byte = fl - 2 + 127;
+    return (uint32_t)min(max(byte, 0), 254);
+}
+
+// 2^(127 - byte); byte <= 252 for any finite fp32 amax, so this is normal.
+__device__ __forceinline__ float mx_inv_scale(uint32_t byte)
+{
+    return __uint_as_float((254u - byte) << 23);
+}
+
+__device__ __forceinline__ uint32_t e2m1_encode(float v, float inv_scale)
+{
+    float m = fabsf(v) * inv_scale;
+    // midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5: a tie moves up only when the
+    // upper neighbour has the even code
+    uint32_t idx = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) +
+                   (m > 2.5f) + (m >= 3.5f) + (m > 5.0f);
+    return ((__float_as_uint(v) >> 31) << 3) | idx;
+}
+
+// 8 lanes per 32-element block, 4 values per lane.
 __global__ __launch_bounds__(256) void quantize_rows_kernel(long nblocks, const float* __restrict__ v,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales)
@@ -69,10 +99,7 @@ void launch_zero(float* y, size_t n, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
-// Slot -> expert (same rule as the fp32 path); false as well for the light
-// experts (at most a.mx_light tokens) when the GEMVs take them: always when
-// the slots are segment heads, with an active list when its light list is
-// not empty (active_list_kernel lists all of them or none).
+// Slot -> expert (same rule as the fp32 path).
 __device__ __forceinline__ bool mx_slot_expert(const FfnArgs& a, int slot, int& e, int& r_beg, int& n_e)
 {
     if (a.active) {
@@ -85,9 +112,7 @@ __device__ __forceinline__ bool mx_slot_expert(const FfnArgs& a, int slot, int& 
     }
     r_beg = a.offsets[e];
     n_e = a.offsets[e + 1] - r_beg;
-    if (n_e <= 0) return false;
-    const bool gemv_light = !a.light_list || a.light_list[a.E] > 0;
-    return !(gemv_light && n_e <= a.mx_light);
+    return n_e > 0;
 }
 
 __device__ __forceinline__ i32x8 op4(uint4 q)
@@ -726,10 +751,10 @@ __device__ __forceinline__ void down_mx_item(const FfnArgs& a, int e, int r_beg,
 
 // Work of one gate/up block.  Without pass lists: the (slot, tile) of
 // xcd_tile and all of the slot's passes.  With them, every (slot, tile,
-// pass) is an item: the items of XCD x are its slots (pslot: the heaviest
-// first, balanced over the XCDs) in order, each as tiles x passes with the
-// passes innermost, so the passes of one (slot,
-// tile) -- the same weight rows, streamed for different tokens -- run side
+// pass) is an item: the items of XCD x are its slots (pslot, balanced over
+// the XCDs by passes) in order, each as tiles x passes with the passes
+// innermost, so the passes of one (slot, tile) -- the same weight rows,
+// streamed for different tokens -- run side
 // by side on one XCD and share its L2; a heavy expert's passes no longer run
 // one after another in a single block.  Block b takes its XCD's items b/8,
 // b/8 + cap, ... (cap = the grid's blocks per XCD, sized from an estimate of
@@ -765,7 +790,7 @@ __device__ __forceinline__ void mx_items(const FfnArgs& a, int ntiles, int* scum
         const int npass = scum[lo + 1] - scum[lo], r = pos - scum[lo] * ntiles;
         const int tile = r / npass, pass = r - tile * npass;
         int e, r_beg, n_e;
-        mx_slot_expert(a, a.pslot[x * a.pstride + lo], e, r_beg, n_e);  // an active slot with passes
+        mx_slot_expert(a, a.pslot[x * a.pstride + lo], e, r_beg, n_e);  // an active slot
         __syncthreads();  // the previous item is done with the LDS
         body(e, r_beg, n_e, tile, pass, pass + 1);
     }
@@ -791,17 +816,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ uint32_t rowtok[16 * kPassMT];
     int slot, tile, e, r_beg, n_e;
     if (a.pslot) {
-        // the gate/up GEMM's balanced slot lists (every slot listed has
-        // passes): XCD x takes the d tiles of its slots, one block running
-        // all of a slot's passes
+        // the gate/up GEMM's balanced slot lists: XCD x takes the d tiles of
+        // its slots, one block running all of a slot's passes
         const int x = blockIdx.x % kXcds, pos = blockIdx.x / kXcds, nt = a.d / kDnTile;
         if (pos / nt >= a.passes[kXcds * a.pstride + x]) return;
         slot = a.pslot[x * a.pstride + pos / nt];
         tile = pos % nt;
-        mx_slot_expert(a, slot, e, r_beg, n_e);
-    } else if (!xcd_tile(blockIdx.x, a.nslots, a.d / kDnTile, slot, tile) || !mx_slot_expert(a, slot, e, r_beg, n_e)) {
+    } else if (!xcd_tile(blockIdx.x, a.nslots, a.d / kDnTile, slot, tile)) {
         return;
     }
+    if (!mx_slot_expert(a, slot, e, r_beg, n_e)) return;
     const int tiles = (n_e + 15) >> 4;
     down_mx_item(a, e, r_beg, n_e, tile, 0, (tiles + kPassMT - 1) / kPassMT, lds, rowtok, hqc, hqs, o);
 }

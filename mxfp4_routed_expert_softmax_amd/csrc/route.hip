@@ -776,28 +776,23 @@ void launch_topk_group(int T, int E, int k, double* logits, const float* bias,
 
 // ---------------------------------------------------------------------------
 // Active experts in ascending id (those with at least one token); the count
-// goes to active[E].  With mt > 0 also the MXFP4 pass lists and the list of
-// light experts.  Each active expert needs ceil(tiles / mt) passes of the GEMMs, or
-// none when the GEMVs take it (1 .. light tokens, when at least
-// kMinLightList experts are that light: it goes to light_list, ascending, the
-// count at light_list[E]).  The experts with passes are cut,
-// in list order, into eight runs of near-equal total passes (an expert goes
-// to XCD floor(8 * passes before it / all passes)), so each XCD's share is
-// within one expert's passes of an eighth however the load is skewed
-// (dealing experts to XCDs by list position put up to 1.9 times the mean on
-// one XCD of the skewed 256-token batch).  Per XCD x: pslot[x * pstride + j]
-// = its j-th slot, passes[x * pstride + j] = passes before it (the XCD's
-// total after the last), passes[8 * pstride + x] = its slot count (at most
-// pstride - 1).
+// goes to active[E].  With mt > 0 also the MXFP4 pass lists: each active
+// expert needs ceil(tiles / mt) passes of the GEMMs.  The experts are cut, in
+// list order, into eight runs of near-equal total passes (an expert goes to
+// XCD floor(8 * passes before it / all passes)), so each XCD's share is within
+// one expert's passes of an eighth however the load is skewed (dealing the
+// experts round-robin put 1.6 times the mean on one XCD of the skewed
+// 256-token batch).  Per XCD x: pslot[x * pstride + j] = its j-th slot,
+// passes[x * pstride + j] = passes before it (the XCD's total after the
+// last), passes[8 * pstride + x] = its slot count (at most pstride - 1).
 __global__ __launch_bounds__(1024) void active_list_kernel(int E, const int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ active, int mt, int light,
-                                                           int32_t* __restrict__ light_list,
+                                                           int32_t* __restrict__ active, int mt,
                                                            int32_t* __restrict__ passes,
                                                            int32_t* __restrict__ pslot, int pstride)
 {
     __shared__ int wave_tot[17];
     __shared__ int first[8], base[8], cnt[8], sum[8];
-    __shared__ int rk_np[1024], rk_pos[1024];  // by rank among the experts with passes
+    __shared__ int np_of[1024];  // passes of each slot
     const int e = threadIdx.x;
     const int n = (e < E) ? offsets[e + 1] - offsets[e] : 0;
     const int flag = n > 0;
@@ -806,18 +801,9 @@ __global__ __launch_bounds__(1024) void active_list_kernel(int E, const int32_t*
     if (flag) active[pos] = e;
     if (e == 0) active[E] = total;
     if (mt <= 0) return;
-    int nlight;
-    block_exclusive_scan(flag && n <= light, wave_tot, &nlight);
-    // the GEMVs take the light experts only when there are enough of them to
-    // fill the chip; a few (a skewed batch's tail) cost less inside the GEMMs
-    const int is_light = flag && n <= light && nlight >= kMinLightList;
-    const int lpos = block_exclusive_scan(is_light, wave_tot, &nlight);
-    if (is_light) light_list[lpos] = e;
-    if (e == 0) light_list[E] = nlight;
-    const int np = (flag && !is_light) ? (((n + 15) >> 4) + mt - 1) / mt : 0;
-    int ptot, nheavy;
+    const int np = flag ? (((n + 15) >> 4) + mt - 1) / mt : 0;
+    int ptot;
     const int pre = block_exclusive_scan(np, wave_tot, &ptot);
-    const int rank = block_exclusive_scan(np > 0 ? 1 : 0, wave_tot, &nheavy);
     if (e < 8) {
         first[e] = 0x7fffffff;
         base[e] = 0x7fffffff;
@@ -825,11 +811,10 @@ __global__ __launch_bounds__(1024) void active_list_kernel(int E, const int32_t*
         sum[e] = 0;
     }
     __syncthreads();
-    const int x = np > 0 ? (int)min((8LL * pre) / ptot, 7LL) : 0;
-    if (np > 0) {
-        rk_np[rank] = np;
-        rk_pos[rank] = pos;
-        atomicMin(&first[x], rank);
+    const int x = flag ? (int)min((8LL * pre) / ptot, 7LL) : 0;
+    if (flag) {
+        np_of[pos] = np;
+        atomicMin(&first[x], pos);
         atomicMin(&base[x], pre);
         atomicAdd(&cnt[x], 1);
         atomicAdd(&sum[x], np);
@@ -837,14 +822,14 @@ __global__ __launch_bounds__(1024) void active_list_kernel(int E, const int32_t*
     __syncthreads();
     // the tables hold pstride - 1 = ceil(E / 8) + 8 slots per XCD; a routing
     // that would put more on one XCD (a few huge experts among many one-pass
-    // ones) is dealt round-robin by rank instead
+    // ones) is dealt round-robin instead
     bool fits = true;
 #pragma unroll
     for (int i = 0; i < 8; ++i) fits = fits && cnt[i] <= pstride - 1;
     if (fits) {
-        if (np > 0) {  // an XCD's experts are consecutive among those with passes
-            pslot[x * pstride + rank - first[x]] = pos;
-            passes[x * pstride + rank - first[x]] = pre - base[x];
+        if (flag) {  // an XCD's slots are consecutive
+            pslot[x * pstride + pos - first[x]] = pos;
+            passes[x * pstride + pos - first[x]] = pre - base[x];
         }
         if (e < 8) {
             passes[e * pstride + cnt[e]] = sum[e];
@@ -852,10 +837,10 @@ __global__ __launch_bounds__(1024) void active_list_kernel(int E, const int32_t*
         }
     } else if (e < 8) {
         int c = 0, j = 0;
-        for (; 8 * j + e < nheavy; ++j) {
-            pslot[e * pstride + j] = rk_pos[8 * j + e];
+        for (; 8 * j + e < total; ++j) {
+            pslot[e * pstride + j] = 8 * j + e;
             passes[e * pstride + j] = c;
-            c += rk_np[8 * j + e];
+            c += np_of[8 * j + e];
         }
         passes[e * pstride + j] = c;
         passes[8 * pstride + e] = j;
@@ -866,11 +851,10 @@ __global__ __launch_bounds__(1024) void active_list_kernel(int E, const int32_t*
 // the experts by a few when all are active), and the total after them
 int pass_stride(int E) { return (E + 7) / 8 + 9; }
 
-void launch_active_list(int E, const int32_t* offsets, int32_t* active, int mt, int light, int32_t* light_list,
-                        int32_t* passes, int32_t* pslot, int pstride, hipStream_t s)
+void launch_active_list(int E, const int32_t* offsets, int32_t* active, int mt, int32_t* passes, int32_t* pslot,
+                        int pstride, hipStream_t s)
 {
-    k3_launch(active_list_kernel, dim3(1), dim3(1024), s, E, offsets, active, mt, light, light_list, passes, pslot,
-              pstride);
+    k3_launch(active_list_kernel, dim3(1), dim3(1024), s, E, offsets, active, mt, passes, pslot, pstride);
 }
 
 }  // namespace k3

@@ -30,10 +30,8 @@ def tiny():
 CASES = [
     (1, "fp32", ["gateup", "down_combine"]),
     (130, "fp32", ["active_list", "gateup", "down", "combine"]),
-    # MXFP4: the GEMV of the light experts (one or two tokens), then the
-    # matrix-core GEMM of the rest; with one token every expert is light
     (1, "mxfp4", ["quantize", "gateup", "down", "combine"]),
-    (65, "mxfp4", ["active_list", "quantize", "gateup", "gateup", "down", "down", "combine"]),
+    (65, "mxfp4", ["active_list", "quantize", "gateup", "down", "combine"]),
 ]
 
 
@@ -82,6 +80,6 @@ def test_fewer_marks_than_kernels(tiny):
     finally:
         k3.StageMarks.clear()
     torch.cuda.synchronize()
-    assert marks.launched == 7
+    assert marks.launched == 5
     assert marks.kinds() == ["active_list", "quantize"]
     assert np.isfinite(fw.y.cpu().numpy()).all()

@@ -317,10 +317,9 @@ def _check_mx_split(x, ref, dbg, y, tokens, k, get=None, shape=None):
 
 
 @pytest.mark.parametrize("T,k", [(2, 16), (5, 16)])
-def test_tiny_mx_every_expert_light(tiny, T, k):
-    """k = E: every expert holds all T tokens.  T = 2: more pairs than experts
-    (an active list) yet every expert light -- too few of them for the GEMVs,
-    so the matrix-core GEMMs must take them; T = 5: every expert heavy."""
+def test_tiny_mx_k_equals_e(tiny, T, k):
+    """k = E: every expert holds all T tokens, more pairs than experts (an
+    active list in which every expert has the same passes)."""
     sh = tiny["shape"]
     x = synthdata.tokens(sh, T, first=900 + T)
     dbg = _dbg_buffers(T, k, sh.d, sh.f)
@@ -591,11 +590,11 @@ def test_k3_batch_t64(k3layer):
 
 
 @pytest.mark.parametrize("T", [1, 8, 64])
-def test_k3_mx_light_dispatch(k3layer, T):
-    """MXFP4 mode at small batches: experts with one or two tokens take the
-    GEMVs on the quantised activations, heavier ones the matrix-core GEMM
-    (T = 1 and 8: almost every expert is light; T = 64: both kinds in one
-    call).  x_q and h_q on every pair, h and y on every token."""
+def test_k3_mx_small_batches(k3layer, T):
+    """MXFP4 mode at small batches, where nearly every expert holds one or two
+    tokens of a 16-row matrix tile (T = 1 and 8: slots are segment heads;
+    T = 64: an active list with the balanced per-XCD pass lists).  x_q and
+    h_q on every pair, h and y on every token."""
     sh = k3layer["shape"]
     x = synthdata.tokens(sh, T, first=30000 + T)
     dbg = _dbg_buffers(T, sh.k, sh.d, sh.f)
@@ -603,9 +602,7 @@ def test_k3_mx_light_dispatch(k3layer, T):
     ref = oracle.route(x, k3layer["wr"], sh.k)
     assert_route_equal(route, ref)
     c = ref["counts"]
-    _log(f"k3 mx T={T}: {int(((c > 0) & (c <= 2)).sum())} light experts, {int((c > 2).sum())} heavy")
-    if T == 64:
-        assert ((c > 0) & (c <= 2)).any() and (c > 2).any(), "the batch should mix light and heavy experts"
+    _log(f"k3 mx T={T}: {int((c > 0).sum())} active experts, at most {int(c.max())} tokens each")
     _check_mx_split(x, ref, dbg, y, range(T), sh.k, shape=sh)
 
 
