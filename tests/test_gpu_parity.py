@@ -512,6 +512,37 @@ def test_edge_format_mx_split_step(edge, T):
     _check_mx_split(x, ref, dbg, y, range(T), sh.k, get=edge["get"])
 
 
+# ------------------------------------------- adversarial MXFP4 pass lists ---
+# 1024 experts with 512-wide reduction axes (the pipelined matrix-core GEMMs
+# and their per-XCD pass lists), small enough to upload whole
+ADV = synthdata.LayerShape("adv_e1024_f512", d=512, f=512, E=1024, k=2, layer=8)
+
+
+def test_mx_pass_lists_round_robin_fallback():
+    """k3moe_ffn on a routing built by hand: expert 1023 holds every token
+    (14,200: 148 passes of the GEMMs), experts 0..1022 about 14 each (one pass).
+    Eight equal-pass runs would give XCDs 0-6 about 146 experts each, more than
+    a table holds (ceil(E / 8) + 8 = 136), so the pass lists are dealt
+    round-robin instead.  x_q and h_q on every pair, h and y on a token of
+    every expert and on the heavy expert's last rows."""
+    sh, T = ADV, 14200
+    _log("adversarial pass lists: generating 1024 experts")
+    dev = _to_dev_experts(synthdata.all_experts_host(sh))
+    x = synthdata.tokens(sh, T)
+    idx = np.stack([np.full(T, sh.E - 1), np.arange(T) % (sh.E - 1)], axis=1).astype(np.int32)
+    ref = dict(topk_idx=idx, topk_w=np.full((T, 2), 0.5, np.float32))
+    ref.update(oracle.permute(idx, sh.E))
+    route = {n: torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for n, v in ref.items()}
+    dbg = _dbg_buffers(T, sh.k, sh.d, sh.f)
+    yd = torch.full((T, sh.d), float("nan"), dtype=torch.float32, device=DEV)
+    k3.k3moe_ffn(torch.from_numpy(x).to(DEV), dev, route, act_mode="mxfp4", y=yd, dbg=dbg)
+    torch.cuda.synchronize()
+    y = yd.cpu().numpy()
+    assert np.isfinite(y).all(), "y has rows the kernels did not write"
+    toks = list(range(sh.E - 1)) + list(range(T - 120, T))
+    _check_mx_split(x, ref, dbg, y, toks, sh.k, shape=sh)
+
+
 # ----------------------------------------------------------- full layer ---
 @pytest.fixture(scope="module")
 def k3layer():
