@@ -151,10 +151,12 @@ __device__ __forceinline__ void load_frag128(const uint8_t* crow, const uint8_t*
 
 // ---------------------------------------------------------------------------
 // Tile order: the hardware deals consecutive workgroups round-robin to the 8
-// XCDs, each with its own L2.  Experts go round-robin to XCDs (slot s -> XCD
-// s % 8) and each XCD receives the n-tiles of one expert back to back, so an
-// expert's activation rows are read from HBM once and from that XCD's L2 by
-// its other tiles; busy and idle experts spread evenly over the XCDs.
+// XCDs, each with its own L2.  Without pass lists (few pairs: slots are
+// segment heads) experts go round-robin to XCDs (slot s -> XCD s % 8) and
+// each XCD receives the n-tiles of one expert back to back, so an expert's
+// activation rows are read from HBM once and from that XCD's L2 by its other
+// tiles.  With an active list, the pass lists place the experts instead
+// (active_list_kernel: eight runs of equal passes).
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ bool xcd_tile(int bid, int nslots, int ntiles, int& slot, int& tile)
