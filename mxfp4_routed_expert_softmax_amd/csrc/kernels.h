@@ -19,7 +19,7 @@ struct WsLayout {
     size_t chunk_masks;  // uint64 [nch][E]          which chunk tokens chose e
     size_t chunk_base;   // int32  [nch][E]          rows of e before chunk c
     size_t active;       // int32  [E + 1]           active experts, count last
-    size_t passes;       // int32  [16*pstride + 8]  MXFP4 gate/up: pass lists per XCD, then their slots
+    size_t passes;       // int32  [16*pstride + 8]  MXFP4 GEMMs: pass lists per XCD, their counts, then their slots
     size_t rsl_x;        // int8   [kRouterSlices][T][d]  int8 router: slices of x
     size_t rsl_w;        // int8   [kRouterSlices][E][d]  int8 router: slices of W_r
     size_t rsl_xe;       // int32  [T]               int8 router: row exponents of x
